@@ -1,0 +1,11 @@
+"""Oracle package: plain float64 CPU attention, used by tests, the smoke check
+and the benchmark's CPU-baseline leg only. TEST INFRASTRUCTURE ONLY; the
+library never imports it."""
+
+from .attention import (  # noqa: F401
+    attention_reference,
+    attention_rows,
+    attention_weights,
+    causal_keep_mask,
+    default_scale,
+)
