@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused attention forward on one MI355X.
+
+One step = one call of fa_fwd over the whole workload (inputs resident in HBM
+before timing starts).  Default workload: causal bf16 attention, B=1 H=32
+S=16384 D=128 (the long-sequence causal shape with S >= 4096 and D = 128).
+Prints ONE JSON line on stdout; a per-workload table goes to stderr with
+--all.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                  [--all] [--no-cpu-baseline] [--copy-calibration]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOPS (bf16, causal) and % of MI355X bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X published dense bf16 matrix peak
+PEAK_F32_TFLOPS = 157.3     # MI355X published fp32 matrix peak
+DEFAULT_WORKLOAD = "c4_bf16_causal_1x32x16384x128"
+SRC = os.path.join(ROOT, "exact_attention_67_amd", "csrc", "fa_fwd.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_bf16_c4_hbm_traffic.txt")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_digest() -> str:
+    with open(SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel source for this workload; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        m = re.match(r"^\s*([a-z_]+)\s*:\s*(\S+)", line)
+        if m:
+            kv[m.group(1)] = m.group(2)
+    if kv.get("source_sha256") != source_digest() or kv.get("workload") != workload:
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def time_workload(w, causal, steps, warmup):
+    import torch
+    import exact_attention_67_amd as fa
+    from tests import workloads as wl
+
+    q, k, v = wl.make_inputs(w, device="cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    fn = fa.fa_fwd if w.dtype == torch.bfloat16 else fa.fa_fwd_f32
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+            w.B, w.H, w.S, w.D, int(causal), w.scale, stream.cuda_stream)
+
+    def step():
+        st = fn(*args)
+        if st != fa.FA_OK:
+            raise fa.FAError(st, fn.__name__)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Whole timed region: exactly `steps` back-to-back launches.
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for _ in range(steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t0.elapsed_time(t1)
+
+    # Per-launch durations: an event pair around each launch on the same
+    # stream (separate pass, so the pairs do not perturb the timed region).
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for a, b in evs:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) for a, b in evs)
+    return dict(total_ms=total_ms, wall_s=wall, ms_per_step=total_ms / steps,
+                launch_ms_avg=sum(per) / len(per), launch_ms_min=per[0],
+                launch_ms_med=per[len(per) // 2])
+
+
+def cpu_baseline(w, causal, budget_s=20.0):
+    """The oracle, as it stands, on the host cores over a bounded sample of the
+    same workload: whole heads (row-blocked), as many as fit the budget."""
+    import torch
+    from oracle import attention as orc
+    from tests import workloads as wl
+
+    threads = max(1, min(16, os.cpu_count() or 1))
+    torch.set_num_threads(threads)
+    q, k, v = wl.make_inputs(w)
+    flops_head = 4.0 * w.S * w.S * w.D * (0.5 if causal else 1.0)
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    done, t_total = 0, 0.0
+    for b, h in heads:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        t = time.perf_counter()
+        orc.attention_reference(q[sl], k[sl], v[sl], causal, w.scale, row_block=2048)
+        t_total += time.perf_counter() - t
+        done += 1
+        if t_total >= budget_s or done >= 8:
+            break
+    return {
+        "value": flops_head * done / t_total / 1e12,
+        "unit": "TFLOP/s",
+        "cores": torch.get_num_threads(),
+        "kind": "oracle",
+        "sample": f"{done} of {len(heads)} heads of {w.name} "
+                  f"({'causal' if causal else 'non-causal'}), float64 torch CPU, "
+                  f"row blocks of 2048, {t_total:.1f} s",
+        "seconds_per_head": t_total / done,
+    }
+
+
+def copy_calibration():
+    """A plain device copy of known size, for scaling rocprofv3 FETCH_SIZE /
+    WRITE_SIZE readings (run under the same --pmc command as the bench)."""
+    import torch
+    n = 256 << 20  # bytes
+    a = torch.empty(n // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"[copy-calibration] copied {n} bytes x3 (read {n}, write {n} per copy)")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--noncausal", action="store_true", help="time the non-causal mask")
+    ap.add_argument("--all", action="store_true", help="also time every workload (stderr)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    a = ap.parse_args()
+
+    if a.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {a.gpus}); "
+              "the forward is independent per (batch, head) and shards by head without "
+              "collectives, but no multi-GPU path is built.", file=sys.stderr)
+        sys.exit(2)
+    rank = int(os.environ.get("RANK", "0"))
+
+    import torch
+    from tests import workloads as wl
+    if not torch.cuda.is_available():
+        log("bench.py: no GPU visible")
+        sys.exit(1)
+    import exact_attention_67_amd as fa
+    fa.load()
+
+    if a.copy_calibration:
+        copy_calibration()
+
+    w = wl.WORKLOADS[a.workload]
+    causal = (not a.noncausal) and (True in w.causal)
+    log(f"[bench] {w.name} causal={causal} steps={a.steps} warmup={a.warmup}")
+    r = time_workload(w, causal, a.steps, a.warmup)
+    flops = w.flops(causal)
+    value = flops / (r["ms_per_step"] * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == torch.bfloat16 else PEAK_F32_TFLOPS
+    achieved = flops / (r["launch_ms_avg"] * 1e-3) / 1e12
+    log(f"[bench] ms/step={r['ms_per_step']:.4f} launch avg={r['launch_ms_avg']:.4f} "
+        f"min={r['launch_ms_min']:.4f} -> {value:.1f} TFLOP/s ({100 * value / peak:.1f}% of peak)")
+
+    if a.all:
+        log(f"{'workload':40s} {'mask':7s} {'ms':>9s} {'TFLOP/s':>9s} {'%peak':>6s}")
+        for name in wl.ORDER:
+            ww = wl.WORKLOADS[name]
+            for c in ww.causal:
+                rr = time_workload(ww, c, max(5, a.steps // 2), 3)
+                pk = PEAK_BF16_TFLOPS if ww.dtype == torch.bfloat16 else PEAK_F32_TFLOPS
+                tf = ww.flops(c) / (rr["launch_ms_avg"] * 1e-3) / 1e12
+                log(f"{name:40s} {'causal' if c else 'full':7s} {rr['launch_ms_avg']:9.4f} "
+                    f"{tf:9.1f} {100 * tf / pk:6.1f}")
+
+    cpu = None
+    if rank == 0 and not a.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample ...")
+        cpu = cpu_baseline(w, causal, a.cpu_budget)
+        log(f"[bench] cpu oracle: {cpu['value'] * 1e3:.1f} GFLOP/s on {cpu['cores']} threads")
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(r["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "S": w.S, "D": w.D,
+                   "causal": causal, "scale": w.scale, "parallelism": "single-gpu"},
+        "pct_of_peak": round(100 * value / peak, 2),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": recorded_traffic(w.name),
+            "kernel": "fa_fwd_bf16_kernel" if w.dtype == torch.bfloat16 else "fa_fwd_f32_kernel",
+            "launch_ms_avg": round(r["launch_ms_avg"], 5),
+            "flops_per_launch": flops,
+        },
+        "cpu_baseline": cpu,
+    }
+    if rank == 0:
+        print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,90 @@
+"""ctypes binding of the C ABI declared in include/fa.h.
+
+Argument marshalling only: every step of the attention forward runs in the HIP
+kernels of libfa_mi355x.so.  There is no fallback of any kind: if the library
+is missing or cannot be loaded, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_NAME = "libfa_mi355x.so"
+LIB_PATH = os.path.join(PKG, LIB_NAME)
+
+# Mirrors enum fa_status in include/fa.h.
+FA_OK = 0
+FA_ERR_NULL = 1
+FA_ERR_SHAPE = 2
+FA_ERR_HEADDIM = 3
+FA_ERR_SCALE = 4
+FA_ERR_CAUSAL = 5
+FA_ERR_ALIGN = 6
+FA_ERR_ALIAS = 7
+FA_ERR_LAUNCH = 8
+
+EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_status_str", "fa_abi_version")
+ABI_VERSION = 1
+
+_lock = threading.Lock()
+_lib = None
+
+
+class FAError(RuntimeError):
+    """A non-zero fa_status returned by the library."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({status_str(status)})")
+
+
+def _declare(lib: ctypes.CDLL) -> None:
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    sig = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
+    lib.fa_fwd.argtypes = sig
+    lib.fa_fwd.restype = i
+    lib.fa_fwd_f32.argtypes = sig
+    lib.fa_fwd_f32.restype = i
+    lib.fa_status_str.argtypes = [i]
+    lib.fa_status_str.restype = ctypes.c_char_p
+    lib.fa_abi_version.argtypes = []
+    lib.fa_abi_version.restype = i
+
+
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load (once) and return the HIP library; raises if it is not built."""
+    global _lib
+    with _lock:
+        if _lib is not None and path is None:
+            return _lib
+        p = path or LIB_PATH
+        if not os.path.exists(p):
+            raise RuntimeError(
+                f"{p} is not built; run `python -m exact_attention_67_amd.build` "
+                "(there is no fallback path)")
+        lib = ctypes.CDLL(p)
+        _declare(lib)
+        if lib.fa_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"{p}: ABI version {lib.fa_abi_version()} != {ABI_VERSION}")
+        if path is None:
+            _lib = lib
+        return lib
+
+
+def status_str(status: int) -> str:
+    return load().fa_status_str(int(status)).decode()
+
+
+def fa_fwd(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, S: int, D: int,
+           causal: int, scale: float, stream: int | None) -> int:
+    """Raw C call on device addresses (ints).  Returns the fa_status."""
+    return load().fa_fwd(q, k, v, o, lse, B, H, S, D, causal, scale, stream)
+
+
+def fa_fwd_f32(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, S: int, D: int,
+               causal: int, scale: float, stream: int | None) -> int:
+    """Raw C call on device addresses (ints).  Returns the fa_status."""
+    return load().fa_fwd_f32(q, k, v, o, lse, B, H, S, D, causal, scale, stream)

@@ -1,0 +1,606 @@
+// Fused, tiled, exact attention forward for MI355X (gfx950, CDNA4).
+//
+// One workgroup of 4 wavefronts owns one (query tile of 128 rows, head,
+// batch); each wavefront owns 32 query rows.  Key/value tiles are streamed
+// through LDS with a running (online) softmax, so the seq x seq score matrix
+// only ever exists in registers -- the method of "Profiling in PyTorch
+// (Part 3): Attention is all you profile", section "Why flash attention
+// exists", with the FlashAttention-2 choices listed in the "FlashAttention-2"
+// blog, section "FlashAttention-2 Optimizations": causal tiles that are fully
+// masked are skipped, the grid runs over sequence blocks as well as batch and
+// heads, and the work is split between waves by query rows so that no
+// cross-wave reduction is needed.  The "Pipelining GmemCopy on kHeadDim" issue
+// discusses overlapping the global-memory copy of the next key block with the
+// math on the current one; here the next K/V tile is fetched into registers
+// while the current one is consumed from the other half of a double-buffered
+// LDS stage.
+//
+// gfx950 mapping (bf16 path):
+//  * Both contractions run on v_mfma_f32_32x32x16_bf16 in transposed form:
+//    S^T = K * Q^T and O^T = V^T * P^T.  In the 32x32 accumulator layout a lane
+//    holds one column (= one query) and 16 rows (= keys or head-dim entries),
+//    so a query's row max / row sum is an in-lane reduction plus one exchange
+//    between lane l and lane l^32, and the per-query rescale factor multiplies
+//    the lane's own O^T column.
+//  * The 32 K rows fed to one MFMA are loaded in a permuted order (bits 2 and 3
+//    of the row index swapped).  With that order the first 8 accumulator
+//    registers of a lane hold 8 consecutive keys, so after the softmax a
+//    lane's registers are directly the B operand of the P*V MFMA.
+//  * V is transposed in registers on its way into LDS (key-contiguous rows),
+//    so the A operand of O^T = V^T * P^T is one 16-byte LDS read per lane.
+//  * LDS rows are XOR-swizzled in 16-byte units so the MFMA operand reads and
+//    the staging writes are free of bank conflicts.
+//  * exp2 with the scale folded into one FMA per score.  The rescale of the
+//    O accumulator is skipped (wave-uniform branch) on tiles where no row's
+//    running max grows, which is most tiles of a long sequence.  The reference
+//    max always equals the running max, so a row's largest weight is exactly
+//    1 and rounds to bf16 without error.
+//  * The 1-D grid is decoded XCD-aware (the 8 XCDs receive workgroups round-
+//    robin; consecutive logical tiles of the same heads are kept on one XCD so
+//    they share its L2) and, when causal, heaviest query tiles first.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "fa.h"
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRowsPerWave = 32;
+constexpr int kBr = kRowsPerWave * kWaves;  // query rows per workgroup
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ float other_half(float x) {
+  // value held by lane l ^ 32 (the other 32-lane half of the wavefront)
+  return __shfl_xor(x, 32);
+}
+
+// Logical workgroup index from the hardware one: workgroup i is dispatched to
+// XCD i % 8; give each XCD a contiguous range of logical indices.
+__device__ __forceinline__ int xcd_logical_index(int i, int n) {
+  const int x = i & 7, s = i >> 3;
+  const int base = n >> 3, rem = n & 7;
+  return x * base + (x < rem ? x : rem) + s;
+}
+
+// Logical index -> (bh, query tile).  Heads are taken in groups of
+// `group_heads`; inside a group the tiles of its heads are interleaved, and
+// when causal the heaviest (last) query tiles come first.
+template <bool CAUSAL>
+__device__ __forceinline__ void decode_tile(int L, int nq, int bh_total, int group_heads,
+                                            int& bh, int& qt) {
+  const int gsize = group_heads * nq;
+  const int grp = L / gsize;
+  const int r = L - grp * gsize;
+  const int left = bh_total - grp * group_heads;
+  const int hin = left < group_heads ? left : group_heads;
+  bh = grp * group_heads + r % hin;
+  const int rank = r / hin;
+  qt = CAUSAL ? (nq - 1 - rank) : rank;
+}
+
+// ----------------------------------------------------------------------------
+// bf16 kernel
+// ----------------------------------------------------------------------------
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+template <int D_, int BC_>
+struct BfCfg {
+  static constexpr int D = D_;
+  static constexpr int BC = BC_;                       // keys per tile
+  static constexpr int KCH = D / 16;                   // MFMA k-steps of Q*K^T
+  static constexpr int KB = BC / 32;                   // 32-key blocks per tile
+  static constexpr int DB = D / 32;                    // 32-row blocks of O^T
+  static constexpr int PCH = BC / 16;                  // MFMA k-steps of P*V
+  static constexpr int ROW_BYTES = D * 2;              // one K or V row in LDS
+  static constexpr int TILE_BYTES = BC * ROW_BYTES;    // K tile or V tile
+  static constexpr int STAGE_BYTES = 2 * TILE_BYTES;   // K then V
+  static constexpr int LDS_BYTES = 2 * STAGE_BYTES;    // double-buffered
+  static constexpr int RC = D / 8;                     // 16-byte chunks per row
+  static constexpr int ROWS_PER_LOAD = 64 / RC;        // rows per 1 KiB wave load
+  static constexpr int LOADS_PER_TILE = TILE_BYTES / 1024;
+  static constexpr int LOADS_PER_WAVE = LOADS_PER_TILE / kWaves;  // per tensor
+  static_assert(TILE_BYTES % (1024 * kWaves) == 0, "tile must split into 1 KiB wave loads");
+  static_assert(D % 32 == 0 && BC % 32 == 0 && D >= 64 && RC <= 64, "tile shape");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+};
+
+// 16-byte chunk swizzles (physical chunk = logical chunk ^ swizzle(row)).
+// K rows are read 16 bytes per lane by 8-lane groups over rows
+// {0,1,2,3,8,9,10,11}+4i of a 32-row block: use bits 0, 1 and 3 of the row.
+__device__ __forceinline__ int kswz(int r) { return (r & 3) | ((r >> 1) & 4); }
+// V rows are read by the 16-lane transposing read over 4 consecutive rows and
+// two adjacent chunks: spread the 4 rows over the 8 chunk slots of a bank line.
+__device__ __forceinline__ int vswz(int r) { return (r & 3) << 1; }
+
+// MFMA row m of a 32-key block reads key row perm(m): bits 2 and 3 swapped.
+__device__ __forceinline__ int key_perm(int m) {
+  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+
+// Asynchronous copy of one K or V tile (rows k0 .. k0+BC-1) from global memory
+// straight into LDS: each wave issues LOADS_PER_WAVE 1 KiB transfers in which
+// lane l fills bytes l*16 .. l*16+15.  Rows past the end of the sequence are
+// clamped to the last row (finite data; those keys are masked).
+template <class C, bool IS_V>
+__device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ src, lds_u8* dst, int k0,
+                                           int S, int wave, int lane) {
+#pragma unroll
+  for (int u = 0; u < C::LOADS_PER_WAVE; ++u) {
+    const int n = wave * C::LOADS_PER_WAVE + u;  // which 1 KiB piece of the tile
+    const int row = n * C::ROWS_PER_LOAD + lane / C::RC;
+    const int pch = lane % C::RC;
+    const int lch = pch ^ (IS_V ? vswz(row) : kswz(row));
+    const int key = min(k0 + row, S - 1);
+    const uint16_t* g = src + (size_t)key * C::D + lch * 8;
+    __builtin_amdgcn_global_load_lds(g, dst + n * 1024, 16, 0, 0);
+  }
+}
+
+template <int D, int BC, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 2) void fa_fwd_bf16_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
+    int S, int nq, int bh_total, int group_heads, float c) {
+  using C = BfCfg<D, BC>;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[C::LDS_BYTES];
+  lds_u8* smem = (lds_u8*)smem_raw;
+
+  int bh, qt;
+  decode_tile<CAUSAL>(xcd_logical_index(blockIdx.x, nq * bh_total), nq, bh_total,
+                      group_heads, bh, qt);
+
+  const size_t head = (size_t)bh * (size_t)S * D;
+  const uint16_t* Qh = Q + head;
+  const uint16_t* Kh = K + head;
+  const uint16_t* Vh = V + head;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int m = lane & 31;   // column of the 32x32 accumulator = query
+  const int hh = lane >> 5;  // lane half
+  const int q0 = qt * kBr;
+  const int qw0 = q0 + wave * kRowsPerWave;
+  const int my_q = qw0 + m;
+  const bool wave_active = qw0 < S;
+
+  // Key tiles this workgroup visits, and the last key this wave needs.
+  const int kend = CAUSAL ? min(S, q0 + kBr) : S;
+  const int ntiles = (kend + BC - 1) / BC;
+  const int wave_klast = CAUSAL ? min(qw0 + kRowsPerWave - 1, S - 1) : (S - 1);
+
+  // Start the first K/V tile while Q is fetched.
+  issue_tile<C, false>(Kh, smem, 0, S, wave, lane);
+  issue_tile<C, true>(Vh, smem + C::TILE_BYTES, 0, S, wave, lane);
+
+  // Q fragments (B operand of S^T = K * Q^T): lane holds Q[my_q][ch*16 + hh*8 .. +8].
+  bf16x8 qf[C::KCH];
+#pragma unroll
+  for (int ch = 0; ch < C::KCH; ++ch) {
+    u32x4 raw = u32x4{0u, 0u, 0u, 0u};
+    if (my_q < S) raw = *reinterpret_cast<const u32x4*>(Qh + (size_t)my_q * D + ch * 16 + hh * 8);
+    qf[ch] = __builtin_bit_cast(bf16x8, raw);
+  }
+
+  // Per-lane byte offsets of the operand reads inside a stage.
+  // K (A operand of S^T): row perm(m), logical chunk 2*ch + hh.
+  const int pm = key_perm(m);
+  const int ksw = kswz(pm);
+  int k_off[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) k_off[b] = pm * C::ROW_BYTES + (((2 * b + hh) ^ ksw) << 4);
+  // V (A operand of O^T, via the transposing read): inside each 16-lane group,
+  // source lane 4j+t points at V[key base + hh*8 + j][d base + 16*(g&1) + 4t].
+  const int g = lane >> 4, j4 = (lane >> 2) & 3, t4 = lane & 3;
+  const int vx = (2 * (g & 1) + (t4 >> 1)) ^ vswz(j4);  // chunk within an even 4-chunk pair
+  const int v_base = (hh * 8 + j4) * C::ROW_BYTES + (t4 & 1) * 8;
+  const int v_off_even = v_base + (vx << 4);         // for d blocks db with db % 2 == 0
+  const int v_off_odd = v_base + ((vx ^ 4) << 4);    // db % 2 == 1
+
+  f32x16 acc[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
+  float m_run = -INFINITY;  // running max of the raw (unscaled) scores
+  float l_part = 0.0f;      // this lane's share of the softmax denominator
+
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  for (int j = 0; j < ntiles; ++j) {
+    const int k0 = j * BC;
+    const lds_u8* Ks = smem + (j & 1) * C::STAGE_BYTES;
+    const lds_u8* Vs = Ks + C::TILE_BYTES;
+    if (j + 1 < ntiles) {
+      lds_u8* nxt = smem + ((j + 1) & 1) * C::STAGE_BYTES;
+      issue_tile<C, false>(Kh, nxt, k0 + BC, S, wave, lane);
+      issue_tile<C, true>(Vh, nxt + C::TILE_BYTES, k0 + BC, S, wave, lane);
+    }
+
+    if (wave_active && k0 <= wave_klast) {
+      // ---- S^T = K * Q^T --------------------------------------------------
+      f32x16 s[C::KB];
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
+#pragma unroll
+        for (int ch = 0; ch < C::KCH; ++ch) {
+          const lds_u8* p = Ks + kb * 32 * C::ROW_BYTES + (ch >> 2) * 128 + k_off[ch & 3];
+          const bf16x8 kf = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(p);
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ch], s[kb], 0, 0, 0);
+        }
+      }
+      // Register r of s[kb] holds key k0 + kb*32 + (r/8)*16 + hh*8 + r%8 for query my_q.
+
+      // ---- mask (diagonal and tail tiles only) -----------------------------
+      const bool need_mask = (CAUSAL && (k0 + BC - 1 > qw0)) || (k0 + BC > S);
+      if (need_mask) {
+        const int lim = (CAUSAL ? min(my_q, S - 1) : (S - 1)) - k0 - hh * 8;
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kb * 32 + (r >> 3) * 16 + (r & 7);
+            s[kb][r] = key > lim ? -INFINITY : s[kb][r];
+          }
+      }
+
+      // ---- online softmax ---------------------------------------------------
+      float mt = s[0][0];
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
+      mt = fmaxf(mt, other_half(mt));
+      if (__any(mt > m_run)) {
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2((m_run - m_new) * c);
+        m_run = m_new;
+        l_part *= alpha;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+      }
+      const float mc = (m_run == -INFINITY) ? 0.0f : m_run * c;
+      float rs = 0.0f;
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = fast_exp2(fmaf(s[kb][r], c, -mc));
+          s[kb][r] = p;
+          rs += p;
+        }
+      l_part += rs;
+
+      bf16x8 pf[C::PCH];
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+          for (int t = 0; t < 8; ++t) pf[2 * kb + half][t] = (__bf16)s[kb][half * 8 + t];
+
+      // ---- O^T += V^T * P^T -------------------------------------------------
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int pc = 0; pc < C::PCH; ++pc) {
+          const lds_u8* p = Vs + pc * 16 * C::ROW_BYTES + (db >> 1) * 128 +
+                            ((db & 1) ? v_off_odd : v_off_even);
+          typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+          const s16x4 hi =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * C::ROW_BYTES));
+          const bf16x8 vf = __builtin_bit_cast(
+              bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[pc], acc[db], 0, 0, 0);
+        }
+    }
+
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  if (!wave_active) return;
+  const float l_tot = l_part + other_half(l_part);
+  if (my_q >= S) return;
+  const float inv = 1.0f / l_tot;
+  uint16_t* Orow = O + head + (size_t)my_q * D;
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      // registers gq*4 .. gq*4+3 hold head-dim entries db*32 + gq*8 + hh*4 + 0..3
+      u32x2 pk;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const __bf16 lo = (__bf16)(acc[db][gq * 4 + 2 * t] * inv);
+        const __bf16 hi = (__bf16)(acc[db][gq * 4 + 2 * t + 1] * inv);
+        pk[t] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+                ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+      }
+      *reinterpret_cast<u32x2*>(Orow + db * 32 + gq * 8 + hh * 4) = pk;
+    }
+  if (hh == 0) LSE[(size_t)bh * S + my_q] = (m_run * c + fast_log2(l_tot)) * kLn2;
+}
+
+// ----------------------------------------------------------------------------
+// float32 kernel (v_mfma_f32_32x32x2_f32): same tiling and softmax, float32
+// operands and float32 softmax weights.  Single-buffered LDS, 32-key tiles.
+// ----------------------------------------------------------------------------
+
+template <int D>
+struct F32Cfg {
+  static constexpr int BC = 32;
+  static constexpr int KST = D + 1;  // padded K/V row stride (floats)
+  static constexpr int ELEMS = 2 * BC * KST;
+  static constexpr int DB = D / 32;
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) void fa_fwd_f32_kernel(
+    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+    float* __restrict__ O, float* __restrict__ LSE, int S, int nq, int bh_total,
+    int group_heads, float c) {
+  using C = F32Cfg<D>;
+  constexpr int BC = C::BC;
+  __shared__ float smem[C::ELEMS];
+  float* Ks = smem;
+  float* Vs = smem + BC * C::KST;
+
+  int bh, qt;
+  decode_tile<CAUSAL>(xcd_logical_index(blockIdx.x, nq * bh_total), nq, bh_total,
+                      group_heads, bh, qt);
+  const size_t head = (size_t)bh * (size_t)S * D;
+  const float* Qh = Q + head;
+  const float* Kh = K + head;
+  const float* Vh = V + head;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int m = lane & 31;
+  const int hh = lane >> 5;
+  const int q0 = qt * kBr;
+  const int qw0 = q0 + wave * kRowsPerWave;
+  const int my_q = qw0 + m;
+  const bool wave_active = qw0 < S;
+  const int kend = CAUSAL ? min(S, q0 + kBr) : S;
+  const int ntiles = (kend + BC - 1) / BC;
+  const int wave_klast = CAUSAL ? min(qw0 + kRowsPerWave - 1, S - 1) : (S - 1);
+
+  // B operand of S^T = K * Q^T: lane holds Q[my_q][2*ch + hh].
+  float qf[D / 2];
+#pragma unroll
+  for (int ch = 0; ch < D / 2; ++ch) qf[ch] = (my_q < S) ? Qh[(size_t)my_q * D + 2 * ch + hh] : 0.0f;
+
+  f32x16 acc[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
+  float m_run = -INFINITY;
+  float l_part = 0.0f;
+
+  for (int j = 0; j < ntiles; ++j) {
+    const int k0 = j * BC;
+    __syncthreads();  // previous tile fully consumed
+    for (int e = tid; e < BC * D; e += kThreads) {
+      const int row = e / D, col = e % D;
+      const int key = k0 + row;
+      const bool ok = key < S;
+      Ks[row * C::KST + col] = ok ? Kh[(size_t)key * D + col] : 0.0f;
+      Vs[row * C::KST + col] = ok ? Vh[(size_t)key * D + col] : 0.0f;
+    }
+    __syncthreads();
+    if (!(wave_active && k0 <= wave_klast)) continue;
+
+    // S^T: A = K rows (identity order), lane holds K[k0 + m][2*ch + hh].
+    f32x16 s;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = 0.0f;
+#pragma unroll
+    for (int ch = 0; ch < D / 2; ++ch)
+      s = __builtin_amdgcn_mfma_f32_32x32x2f32(Ks[m * C::KST + 2 * ch + hh], qf[ch], s, 0, 0, 0);
+    // Register r holds key k0 + (r/4)*8 + hh*4 + r%4.
+
+    const bool need_mask = (CAUSAL && (k0 + BC - 1 > qw0)) || (k0 + BC > S);
+    if (need_mask) {
+      const int lim = CAUSAL ? min(my_q, S - 1) : (S - 1);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + (r >> 2) * 8 + hh * 4 + (r & 3);
+        if (key > lim) s[r] = -INFINITY;
+      }
+    }
+    float mt = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[r]);
+    mt = fmaxf(mt, other_half(mt));
+    const bool grow = mt > m_run;
+    if (__any(grow)) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2((m_run - m_new) * c);
+      m_run = m_new;
+      l_part *= alpha;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+    }
+    const float mc = (m_run == -INFINITY) ? 0.0f : m_run * c;
+    float rs = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = fast_exp2(fmaf(s[r], c, -mc));
+      s[r] = p;
+      rs += p;
+    }
+    l_part += rs;
+
+    // O^T += V^T * P^T in 16 steps of 2 keys: step r pairs register r of the
+    // two lane halves, i.e. keys (r/4)*8 + hh*4 + r%4.
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = (r >> 2) * 8 + hh * 4 + (r & 3);
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(Vs[key * C::KST + db * 32 + m], s[r],
+                                                       acc[db], 0, 0, 0);
+      }
+  }
+
+  if (!wave_active) return;
+  const float l_tot = l_part + other_half(l_part);
+  if (my_q >= S) return;
+  const float inv = 1.0f / l_tot;
+  float* Orow = O + head + (size_t)my_q * D;
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) Orow[db * 32 + (r >> 2) * 8 + hh * 4 + (r & 3)] = acc[db][r] * inv;
+  if (hh == 0) LSE[(size_t)bh * S + my_q] = (m_run * c + fast_log2(l_tot)) * kLn2;
+}
+
+// ----------------------------------------------------------------------------
+// Host side: validation and launch
+// ----------------------------------------------------------------------------
+
+bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+struct Plan {
+  int nq;
+  int bh_total;
+  int group_heads;
+  unsigned grid;
+  float c;
+};
+
+int validate(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             int B, int H, int S, int D, int causal, float scale, size_t elem, Plan* plan) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (B < 1 || H < 1 || S < 1) return FA_ERR_SHAPE;
+  if (D != 64 && D != 128 && D != 256) return FA_ERR_HEADDIM;
+  if (causal != 0 && causal != 1) return FA_ERR_CAUSAL;
+  if (!(scale > 0.0f) || !isfinite(scale)) return FA_ERR_SCALE;
+  const int64_t bh = (int64_t)B * H;
+  const int64_t nq = ((int64_t)S + kBr - 1) / kBr;
+  if (bh > INT32_MAX || (int64_t)S * D > INT32_MAX || nq * bh > INT32_MAX) return FA_ERR_SHAPE;
+  const int64_t n = bh * S * D;
+  if ((uint64_t)n > (uint64_t)(SIZE_MAX / elem) / 2) return FA_ERR_SHAPE;
+  const uintptr_t a16 = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o;
+  if ((a16 & 15u) || ((uintptr_t)lse & 3u)) return FA_ERR_ALIGN;
+  const size_t tb = (size_t)n * elem, lb = (size_t)(bh * S) * sizeof(float);
+  if (ranges_overlap(o, tb, q, tb) || ranges_overlap(o, tb, k, tb) ||
+      ranges_overlap(o, tb, v, tb) || ranges_overlap(lse, lb, q, tb) ||
+      ranges_overlap(lse, lb, k, tb) || ranges_overlap(lse, lb, v, tb) ||
+      ranges_overlap(lse, lb, o, tb))
+    return FA_ERR_ALIAS;
+  plan->nq = (int)nq;
+  plan->bh_total = (int)bh;
+  plan->group_heads = bh >= 8 ? (int)(bh / 8) : 1;
+  plan->grid = (unsigned)(nq * bh);
+  plan->c = scale * kLog2e;
+  return FA_OK;
+}
+
+template <class KernelT, class... Args>
+int launch(KernelT kernel, const Plan& p, hipStream_t stream, Args... args) {
+  void* argv[] = {static_cast<void*>(&args)...};
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(p.grid),
+                                       dim3(kThreads), argv, 0, stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+template <int D, int BC>
+int run_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int S,
+             bool causal, const Plan& p, hipStream_t stream) {
+  const uint16_t* Q = static_cast<const uint16_t*>(q);
+  const uint16_t* K = static_cast<const uint16_t*>(k);
+  const uint16_t* V = static_cast<const uint16_t*>(v);
+  uint16_t* Out = static_cast<uint16_t*>(o);
+  if (causal)
+    return launch(fa_fwd_bf16_kernel<D, BC, true>, p, stream, Q, K, V, Out, lse, S, p.nq,
+                  p.bh_total, p.group_heads, p.c);
+  return launch(fa_fwd_bf16_kernel<D, BC, false>, p, stream, Q, K, V, Out, lse, S, p.nq,
+                p.bh_total, p.group_heads, p.c);
+}
+
+template <int D>
+int run_f32(const float* q, const float* k, const float* v, float* o, float* lse, int S,
+            bool causal, const Plan& p, hipStream_t stream) {
+  if (causal)
+    return launch(fa_fwd_f32_kernel<D, true>, p, stream, q, k, v, o, lse, S, p.nq, p.bh_total,
+                  p.group_heads, p.c);
+  return launch(fa_fwd_f32_kernel<D, false>, p, stream, q, k, v, o, lse, S, p.nq, p.bh_total,
+                p.group_heads, p.c);
+}
+
+}  // namespace
+
+extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                      int H, int S, int D, int causal, float scale, void* stream) {
+  Plan p;
+  const int st = validate(q, k, v, o, lse, B, H, S, D, causal, scale, 2, &p);
+  if (st != FA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (D) {
+    case 64: return run_bf16<64, 64>(q, k, v, o, lse, S, causal, p, s);
+    case 128: return run_bf16<128, 64>(q, k, v, o, lse, S, causal, p, s);
+    default: return run_bf16<256, 32>(q, k, v, o, lse, S, causal, p, s);
+  }
+}
+
+extern "C" int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                          int B, int H, int S, int D, int causal, float scale, void* stream) {
+  Plan p;
+  const int st = validate(q, k, v, o, lse, B, H, S, D, causal, scale, 4, &p);
+  if (st != FA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (D) {
+    case 64: return run_f32<64>(q, k, v, o, lse, S, causal, p, s);
+    case 128: return run_f32<128>(q, k, v, o, lse, S, causal, p, s);
+    default: return run_f32<256>(q, k, v, o, lse, S, causal, p, s);
+  }
+}
+
+extern "C" const char* fa_status_str(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "a tensor pointer is NULL";
+    case FA_ERR_SHAPE: return "B, H or S < 1, or a size overflows";
+    case FA_ERR_HEADDIM: return "head dimension must be 64, 128 or 256";
+    case FA_ERR_SCALE: return "scale must be finite and > 0";
+    case FA_ERR_CAUSAL: return "causal must be 0 or 1";
+    case FA_ERR_ALIGN: return "q/k/v/o must be 16-byte aligned and lse 4-byte aligned";
+    case FA_ERR_ALIAS: return "o or lse overlaps an input or each other";
+    case FA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+extern "C" int fa_abi_version(void) { return 1; }

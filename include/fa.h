@@ -1,0 +1,101 @@
+/*
+ * fa.h -- C ABI of a fused, tiled, exact scaled-dot-product attention forward
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (per batch b and head h, for every query row i):
+ *
+ *   scores_ij = scale * sum_d q[b,h,i,d] * k[b,h,j,d]
+ *   causal:     scores_ij = -inf for j > i            (key j kept iff j <= i)
+ *   o[b,h,i,:] = sum_j softmax_j(scores_i.) * v[b,h,j,:]
+ *   lse[b,h,i] = log sum_j exp(scores_ij)              (natural log)
+ *
+ * This is the five-step naive attention (matmul, scale, masked_fill with -inf,
+ * softmax, matmul) of "Profiling in PyTorch (Part 3): Attention is all you
+ * profile", section "Naive attention", with the causal keep-matrix built as a
+ * lower triangle as in that page's "Math backend" section.  It is evaluated
+ * the way that page's "Why flash attention exists" section and the
+ * "FlashAttention-2" blog ("FlashAttention-2 Optimizations": causal masking,
+ * parallelism over sequence length, work split between waves by query rows)
+ * describe: key/value tiles are streamed through on-chip memory with a running
+ * softmax, and the seq x seq score matrix never reaches device memory.  The
+ * per-row log-sum-exp output is not described on the pages; it is the natural
+ * log of the softmax denominator, scale included.
+ *
+ * Layout: q, k, v and o are dense row-major [B, H, S, D] tensors with D
+ * innermost, i.e. element (b,h,s,d) is at ((b*H + h)*S + s)*D + d -- the
+ * [batch, heads, seq, head_dim] layout of the naive-attention listing on the
+ * same page, consumed as-is (no transposes).  lse is dense float32 [B, H, S].
+ * Self-attention only: queries and keys share the one length S.
+ *
+ * Ownership and memory: every pointer is device memory owned by the caller.
+ * The library never allocates, frees or keeps a pointer beyond the call.
+ * q, k, v are only read; o and lse are fully overwritten and never read.
+ * o and lse must not overlap q, k, v or each other.  q, k, v, o must be 16-byte
+ * aligned; lse 4-byte aligned.
+ *
+ * Asynchrony: the work is enqueued on `stream` (a hipStream_t; NULL means the
+ * default stream) and the call returns without synchronising.  The library
+ * keeps no state, so concurrent calls on different streams are safe.
+ *
+ * Errors: arguments are validated on the host before any HIP call.  On a
+ * validation error nothing is enqueued and the outputs are untouched.  The
+ * functions never throw and never print.
+ */
+#ifndef FA_MI355X_H
+#define FA_MI355X_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point (plain int in the ABI). */
+enum fa_status {
+    FA_OK          = 0, /* enqueued */
+    FA_ERR_NULL    = 1, /* a tensor pointer is NULL */
+    FA_ERR_SHAPE   = 2, /* B, H or S < 1, or a size/offset overflows */
+    FA_ERR_HEADDIM = 3, /* D not one of 64, 128, 256 */
+    FA_ERR_SCALE   = 4, /* scale not finite or not > 0 */
+    FA_ERR_CAUSAL  = 5, /* causal not 0 or 1 */
+    FA_ERR_ALIGN   = 6, /* q/k/v/o not 16-byte aligned or lse not 4-byte aligned */
+    FA_ERR_ALIAS   = 7, /* o or lse overlaps an input or each other */
+    FA_ERR_LAUNCH  = 8  /* the HIP launch itself failed */
+};
+
+/*
+ * fa_fwd -- bf16 attention forward.
+ *   q, k, v : bf16 [B,H,S,D] inputs (device).
+ *   o       : bf16 [B,H,S,D] output (device), rounded to nearest even from the
+ *             float32 accumulator.
+ *   lse     : float32 [B,H,S] output (device), natural-log log-sum-exp.
+ *   B, H, S : batch, heads, sequence length (>= 1).
+ *   D       : head dimension, one of 64, 128, 256.
+ *   causal  : 1 = key j visible to query i iff j <= i; 0 = all keys.
+ *   scale   : score multiplier, finite and > 0 (usually 1/sqrt(D)).
+ *   stream  : hipStream_t to enqueue on (NULL = default stream).
+ * Arithmetic: bf16 products with float32 accumulation for both contractions;
+ * the softmax (running max, exponentials, running sum) is float32; the softmax
+ * weights are rounded to bf16 before they multiply v.
+ * Returns an fa_status value.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int S, int D, int causal, float scale, void* stream);
+
+/*
+ * fa_fwd_f32 -- the same operation on float32 q, k, v, o.  All arithmetic is
+ * float32 (float32 matrix-core products and accumulation, float32 softmax
+ * weights).  Arguments, layout, ownership and errors as for fa_fwd.
+ */
+int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+               int B, int H, int S, int D, int causal, float scale, void* stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* fa_status_str(int status);
+
+/* ABI version of this library; bumped on any incompatible change. */
+int fa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_H */
