@@ -98,7 +98,14 @@ __device__ __forceinline__ void decode_tile(int L, int nq, int bh_total, int gro
 // ----------------------------------------------------------------------------
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+
+// A row's reference max is only raised when its running max exceeds it by
+// more than this many powers of two, so softmax weights stay <= 2^8.
+constexpr float kRescaleThreshold = 8.0f;
 
 template <int D_, int BC_>
 struct BfCfg {
@@ -110,57 +117,129 @@ struct BfCfg {
   static constexpr int PCH = BC / 16;                  // MFMA k-steps of P*V
   static constexpr int ROW_BYTES = D * 2;              // one K or V row in LDS
   static constexpr int TILE_BYTES = BC * ROW_BYTES;    // K tile or V tile
-  static constexpr int STAGE_BYTES = 2 * TILE_BYTES;   // K then V
-  static constexpr int LDS_BYTES = 2 * STAGE_BYTES;    // double-buffered
+  static constexpr int LDS_BYTES = 4 * TILE_BYTES;     // 2 K + 2 V buffers
   static constexpr int RC = D / 8;                     // 16-byte chunks per row
   static constexpr int ROWS_PER_LOAD = 64 / RC;        // rows per 1 KiB wave load
-  static constexpr int LOADS_PER_TILE = TILE_BYTES / 1024;
-  static constexpr int LOADS_PER_WAVE = LOADS_PER_TILE / kWaves;  // per tensor
+  static constexpr int LOADS_PER_WAVE = TILE_BYTES / 1024 / kWaves;  // per tensor
+  // LDS bank geometry: 64 banks of 4 bytes, i.e. 256-byte bank lines.
+  static constexpr int ROWS_PER_LINE = 256 / ROW_BYTES > 1 ? 256 / ROW_BYTES : 1;
+  static constexpr int CH_PER_LINE = 16;               // 16-byte chunks per bank line
+  static constexpr int NKOFF = KCH < 8 ? KCH : 8;      // distinct K read offsets
+  static constexpr int NVOFF = DB < 4 ? DB : 4;        // distinct V read offsets
   static_assert(TILE_BYTES % (1024 * kWaves) == 0, "tile must split into 1 KiB wave loads");
   static_assert(D % 32 == 0 && BC % 32 == 0 && D >= 64 && RC <= 64, "tile shape");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
-// 16-byte chunk swizzles (physical chunk = logical chunk ^ swizzle(row)).
-// K rows are read 16 bytes per lane by 8-lane groups over rows
-// {0,1,2,3,8,9,10,11}+4i of a 32-row block: use bits 0, 1 and 3 of the row.
-__device__ __forceinline__ int kswz(int r) { return (r & 3) | ((r >> 1) & 4); }
-// V rows are read by the 16-lane transposing read over 4 consecutive rows and
-// two adjacent chunks: spread the 4 rows over the 8 chunk slots of a bank line.
-__device__ __forceinline__ int vswz(int r) { return (r & 3) << 1; }
+// 16-byte chunk swizzles (physical chunk = logical chunk ^ swizzle(row)), for
+// an LDS of 64 four-byte banks (a 16-lane group of 16-byte reads, or a
+// 32-lane group of 8-byte reads, is served per pass).
+// K: a 16-lane group reads one chunk column of 16 different rows of a 32-row
+// block -> the 16 rows of a bank line's worth must land in 16 distinct chunk
+// slots: XOR with the row index among the rows that share a line position.
+template <class C>
+__device__ __forceinline__ int kswz(int r) {
+  return (r / C::ROWS_PER_LINE) & (C::CH_PER_LINE / C::ROWS_PER_LINE - 1);
+}
+// V: a 32-lane pass of the transposing read covers 4 consecutive rows x 64
+// bytes (4 chunks): shift each row's 4-chunk group to its own slot.
+template <class C>
+__device__ __forceinline__ int vswz(int r) {
+  constexpr int groups = (C::CH_PER_LINE / C::ROWS_PER_LINE) / 4;  // 4-chunk slots per row
+  return ((r / C::ROWS_PER_LINE) & (groups - 1)) << 2;
+}
 
 // MFMA row m of a 32-key block reads key row perm(m): bits 2 and 3 swapped.
 __device__ __forceinline__ int key_perm(int m) {
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
 
-// Asynchronous copy of one K or V tile (rows k0 .. k0+BC-1) from global memory
-// straight into LDS: each wave issues LOADS_PER_WAVE 1 KiB transfers in which
-// lane l fills bytes l*16 .. l*16+15.  Rows past the end of the sequence are
-// clamped to the last row (finite data; those keys are masked).
+// The value held by lane l ^ 32, through the gfx950 lane-half swap.
+__device__ __forceinline__ float swap_halves(float x, int hh) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                                  __builtin_bit_cast(unsigned, x), false, false);
+  return __builtin_bit_cast(float, hh ? r[0] : r[1]);
+}
+
+// Per-lane element offsets (within one head, tile starting at key 0) of the
+// 16-byte pieces this lane copies; row r of the tile lands in LDS row r with
+// its chunks swizzled.
 template <class C, bool IS_V>
-__device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ src, lds_u8* dst, int k0,
-                                           int S, int wave, int lane) {
+__device__ __forceinline__ void tile_offsets(int* off, int* row, int wave, int lane) {
 #pragma unroll
   for (int u = 0; u < C::LOADS_PER_WAVE; ++u) {
-    const int n = wave * C::LOADS_PER_WAVE + u;  // which 1 KiB piece of the tile
-    const int row = n * C::ROWS_PER_LOAD + lane / C::RC;
-    const int pch = lane % C::RC;
-    const int lch = pch ^ (IS_V ? vswz(row) : kswz(row));
-    const int key = min(k0 + row, S - 1);
-    const uint16_t* g = src + (size_t)key * C::D + lch * 8;
-    __builtin_amdgcn_global_load_lds(g, dst + n * 1024, 16, 0, 0);
+    const int n = wave * C::LOADS_PER_WAVE + u;
+    const int r = n * C::ROWS_PER_LOAD + lane / C::RC;
+    const int lch = (lane % C::RC) ^ (IS_V ? vswz<C>(r) : kswz<C>(r));
+    row[u] = r;
+    off[u] = r * C::D + lch * 8;
   }
 }
 
+// Asynchronous global -> LDS copy of one K or V tile: this wave issues
+// LOADS_PER_WAVE transfers of 1 KiB, lane l filling bytes 16l .. 16l+15 (a
+// wave-uniform base address plus a per-lane 32-bit offset).  In the last
+// (partial) tile, rows past the sequence end are clamped to the last row:
+// finite data whose keys are masked.
+template <class C>
+__device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ head_src, lds_u8* dst,
+                                           int k0, int S, int wave, const int* off,
+                                           const int* row) {
+  const char* base = (const char*)(head_src + (size_t)k0 * C::D);
+  lds_u8* lds = dst + wave * (C::LOADS_PER_WAVE * 1024);
+  if (k0 + C::BC <= S) {
+#pragma unroll
+    for (int u = 0; u < C::LOADS_PER_WAVE; ++u) {
+      const void* gp = base + (uint32_t)(off[u] * 2);
+      lds_u8* lp = lds + u * 1024;
+      __builtin_amdgcn_global_load_lds(gp, lp, 16, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < C::LOADS_PER_WAVE; ++u) {
+      const int o = off[u] - (row[u] - min(row[u], S - 1 - k0)) * C::D;
+      const void* gp = base + (uint32_t)(o * 2);
+      lds_u8* lp = lds + u * 1024;
+      __builtin_amdgcn_global_load_lds(gp, lp, 16, 0, 0);
+    }
+  }
+}
+
+// S^T (keys x queries) for one tile: s[kb] = K[kb*32 + perm(m)][:] . Q[my_q][:]
+template <class C>
+__device__ __forceinline__ void qk_tile(f32x16 (&s)[C::KB], const lds_u8* Ks,
+                                        const bf16x8 (&qf)[C::KCH], const int (&k_off)[C::NKOFF]) {
+#pragma unroll
+  for (int kb = 0; kb < C::KB; ++kb) {
+#pragma unroll
+    for (int ch = 0; ch < C::KCH; ++ch) {
+      const bf16x8 kf = *(const lds_bf16x8*)(Ks + kb * 32 * C::ROW_BYTES +
+                                              (ch / C::NKOFF) * 256 + k_off[ch % C::NKOFF]);
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ch], ch == 0 ? f32x16{} : s[kb], 0,
+                                                      0, 0);
+    }
+  }
+}
+
+// Two waves per SIMD up to D = 128; D = 256 needs the full register file.
 template <int D, int BC, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void fa_fwd_bf16_kernel(
+__global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void fa_fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
     int S, int nq, int bh_total, int group_heads, float c) {
   using C = BfCfg<D, BC>;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[C::LDS_BYTES];
-  lds_u8* smem = (lds_u8*)smem_raw;
+  // Four separate buffers (K and V, two each) rather than one array indexed
+  // by tile parity: every access below names its buffer statically, so the
+  // compiler can tell that an asynchronous copy into one buffer never aliases
+  // reads of another and does not make those reads wait for the copy.
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf0_raw[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf1_raw[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vbuf0_raw[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vbuf1_raw[C::TILE_BYTES];
+  lds_u8* kbuf0 = (lds_u8*)kbuf0_raw;
+  lds_u8* kbuf1 = (lds_u8*)kbuf1_raw;
+  lds_u8* vbuf0 = (lds_u8*)vbuf0_raw;
+  lds_u8* vbuf1 = (lds_u8*)vbuf1_raw;
 
   int bh, qt;
   decode_tile<CAUSAL>(xcd_logical_index(blockIdx.x, nq * bh_total), nq, bh_total,
@@ -173,22 +252,28 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_bf16_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m = lane & 31;   // column of the 32x32 accumulator = query
   const int hh = lane >> 5;  // lane half
   const int q0 = qt * kBr;
   const int qw0 = q0 + wave * kRowsPerWave;
   const int my_q = qw0 + m;
-  const bool wave_active = qw0 < S;
 
-  // Key tiles this workgroup visits, and the last key this wave needs.
+  // Key tiles this workgroup visits, and how many of them this wave needs.
   const int kend = CAUSAL ? min(S, q0 + kBr) : S;
   const int ntiles = (kend + BC - 1) / BC;
   const int wave_klast = CAUSAL ? min(qw0 + kRowsPerWave - 1, S - 1) : (S - 1);
+  const int wave_ntiles = qw0 < S ? min(ntiles, wave_klast / BC + 1) : 0;
 
-  // Start the first K/V tile while Q is fetched.
-  issue_tile<C, false>(Kh, smem, 0, S, wave, lane);
-  issue_tile<C, true>(Vh, smem + C::TILE_BYTES, 0, S, wave, lane);
+  int koff[C::LOADS_PER_WAVE], krow[C::LOADS_PER_WAVE];
+  int voff[C::LOADS_PER_WAVE], vrow[C::LOADS_PER_WAVE];
+  tile_offsets<C, false>(koff, krow, wave, lane);
+  tile_offsets<C, true>(voff, vrow, wave, lane);
+
+  // The K stream runs one tile ahead of the V stream: K(0), K(1), V(0) now.
+  issue_tile<C>(Kh, kbuf0, 0, S, wave, koff, krow);
+  issue_tile<C>(Vh, vbuf0, 0, S, wave, voff, vrow);
+  if (ntiles > 1) issue_tile<C>(Kh, kbuf1, BC, S, wave, koff, krow);
 
   // Q fragments (B operand of S^T = K * Q^T): lane holds Q[my_q][ch*16 + hh*8 .. +8].
   bf16x8 qf[C::KCH];
@@ -199,116 +284,101 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_bf16_kernel(
     qf[ch] = __builtin_bit_cast(bf16x8, raw);
   }
 
-  // Per-lane byte offsets of the operand reads inside a stage.
-  // K (A operand of S^T): row perm(m), logical chunk 2*ch + hh.
+  // Per-lane byte offsets of the operand reads inside a buffer.
+  // K (A operand of S^T): row perm(m), logical chunk 2*ch + hh; chunk bits
+  // above the swizzle go into the immediate offset.
   const int pm = key_perm(m);
-  const int ksw = kswz(pm);
-  int k_off[4];
+  const int ksw = kswz<C>(pm);
+  int k_off[C::NKOFF];
 #pragma unroll
-  for (int b = 0; b < 4; ++b) k_off[b] = pm * C::ROW_BYTES + (((2 * b + hh) ^ ksw) << 4);
+  for (int b = 0; b < C::NKOFF; ++b) k_off[b] = pm * C::ROW_BYTES + (((2 * b + hh) ^ ksw) << 4);
   // V (A operand of O^T, via the transposing read): inside each 16-lane group,
-  // source lane 4j+t points at V[key base + hh*8 + j][d base + 16*(g&1) + 4t].
+  // source lane 4j+t points at V[key base + hh*8 + j][d base + 16*(g&1) + 4t],
+  // i.e. logical chunk 4*db + 2*(g&1) + t/2 of row (hh*8 + j) + 16*pc (+ 4).
   const int g = lane >> 4, j4 = (lane >> 2) & 3, t4 = lane & 3;
-  const int vx = (2 * (g & 1) + (t4 >> 1)) ^ vswz(j4);  // chunk within an even 4-chunk pair
-  const int v_base = (hh * 8 + j4) * C::ROW_BYTES + (t4 & 1) * 8;
-  const int v_off_even = v_base + (vx << 4);         // for d blocks db with db % 2 == 0
-  const int v_off_odd = v_base + ((vx ^ 4) << 4);    // db % 2 == 1
+  const int vx = 2 * (g & 1) + (t4 >> 1);
+  const int vsw = vswz<C>(hh * 8 + j4);  // same for the +4 and +16*pc rows
+  const int v_row = (hh * 8 + j4) * C::ROW_BYTES + (t4 & 1) * 8;
+  int v_off[C::NVOFF];
+#pragma unroll
+  for (int d4 = 0; d4 < C::NVOFF; ++d4) v_off[d4] = v_row + (((4 * d4 + vx) ^ vsw) << 4);
 
   f32x16 acc[C::DB];
 #pragma unroll
-  for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
-  float m_run = -INFINITY;  // running max of the raw (unscaled) scores
-  float l_part = 0.0f;      // this lane's share of the softmax denominator
+  for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
+  float m_run = -INFINITY;  // reference max of the raw (unscaled) scores
+  float l_exact = 0.0f;     // this lane's share of sum(p) with float32 weights
+  float l_round = 0.0f;     // this lane's share of sum(bf16(p)), the weights P*V used
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  // S tiles in two named buffers used alternately (no copy between tiles).
+  f32x16 s_a[C::KB], s_b[C::KB];
+  if (wave_ntiles > 0) qk_tile<C>(s_a, kbuf0, qf, k_off);
+  __syncthreads();  // every wave is done with K(0) before K(2) overwrites it
 
-  for (int j = 0; j < ntiles; ++j) {
-    const int k0 = j * BC;
-    const lds_u8* Ks = smem + (j & 1) * C::STAGE_BYTES;
-    const lds_u8* Vs = Ks + C::TILE_BYTES;
-    if (j + 1 < ntiles) {
-      lds_u8* nxt = smem + ((j + 1) & 1) * C::STAGE_BYTES;
-      issue_tile<C, false>(Kh, nxt, k0 + BC, S, wave, lane);
-      issue_tile<C, true>(Vh, nxt + C::TILE_BYTES, k0 + BC, S, wave, lane);
-    }
-
-    if (wave_active && k0 <= wave_klast) {
-      // ---- S^T = K * Q^T --------------------------------------------------
-      f32x16 s[C::KB];
-#pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
-#pragma unroll
-        for (int ch = 0; ch < C::KCH; ++ch) {
-          const lds_u8* p = Ks + kb * 32 * C::ROW_BYTES + (ch >> 2) * 128 + k_off[ch & 3];
-          const bf16x8 kf = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(p);
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ch], s[kb], 0, 0, 0);
-        }
-      }
-      // Register r of s[kb] holds key k0 + kb*32 + (r/8)*16 + hh*8 + r%8 for query my_q.
-
+  // Iteration j: start K(j+2) and V(j+1); compute S(j+1) into s_out while the
+  // weights of tile j (s_in) form; then O += P(j) V(j).
+  auto step = [&](const int j, lds_u8* k_next, lds_u8* k_load, const lds_u8* v_cur,
+                  lds_u8* v_load, f32x16 (&s_in)[C::KB], f32x16 (&s_out)[C::KB]) {
+    if (j + 2 < ntiles) issue_tile<C>(Kh, k_load, (j + 2) * BC, S, wave, koff, krow);
+    if (j + 1 < ntiles) issue_tile<C>(Vh, v_load, (j + 1) * BC, S, wave, voff, vrow);
+    if (j < wave_ntiles) {
+      const int k0 = j * BC;
       // ---- mask (diagonal and tail tiles only) -----------------------------
-      const bool need_mask = (CAUSAL && (k0 + BC - 1 > qw0)) || (k0 + BC > S);
-      if (need_mask) {
+      if ((CAUSAL && (k0 + BC - 1 > qw0)) || (k0 + BC > S)) {
         const int lim = (CAUSAL ? min(my_q, S - 1) : (S - 1)) - k0 - hh * 8;
 #pragma unroll
         for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = kb * 32 + (r >> 3) * 16 + (r & 7);
-            s[kb][r] = key > lim ? -INFINITY : s[kb][r];
+            s_in[kb][r] = key > lim ? -INFINITY : s_in[kb][r];
           }
       }
-
-      // ---- online softmax ---------------------------------------------------
-      float mt = s[0][0];
+      // ---- tile max; the (rare) move of the reference max ------------------
+      float mt = s_in[0][0];
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
-      mt = fmaxf(mt, other_half(mt));
-      if (__any(mt > m_run)) {
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s_in[kb][r]);
+      mt = fmaxf(mt, swap_halves(mt, hh));
+      // true on the first tile (m_run = -inf); every row has an unmasked key
+      // in tile 0, so no NaN arises here
+      if (__any((mt - m_run) * c > kRescaleThreshold)) {
         const float m_new = fmaxf(m_run, mt);
-        const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2((m_run - m_new) * c);
+        const float alpha = fast_exp2((m_run - m_new) * c);  // 0 on the first tile
         m_run = m_new;
-        l_part *= alpha;
+        l_exact *= alpha;
+        l_round *= alpha;
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+        for (int db = 0; db < C::DB; ++db) acc[db] *= alpha;
       }
-      const float mc = (m_run == -INFINITY) ? 0.0f : m_run * c;
-      float rs = 0.0f;
-#pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(fmaf(s[kb][r], c, -mc));
-          s[kb][r] = p;
-          rs += p;
-        }
-      l_part += rs;
+      const float mc = m_run * c;
 
+      // ---- S(j+1) on the matrix cores (result unused past the last tile) ---
+      qk_tile<C>(s_out, k_next, qf, k_off);
+
+      // ---- weights of tile j: p = 2^(s*c - m*c), rounded to bf16 -------------
+      float rs = 0.0f;
       bf16x8 pf[C::PCH];
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-        for (int half = 0; half < 2; ++half)
-#pragma unroll
-          for (int t = 0; t < 8; ++t) pf[2 * kb + half][t] = (__bf16)s[kb][half * 8 + t];
+        for (int r = 0; r < 16; ++r) {
+          const float p = fast_exp2(fmaf(s_in[kb][r], c, -mc));
+          rs += p;
+          pf[2 * kb + (r >> 3)][r & 7] = (__bf16)p;
+        }
 
       // ---- O^T += V^T * P^T -------------------------------------------------
 #pragma unroll
       for (int db = 0; db < C::DB; ++db)
 #pragma unroll
         for (int pc = 0; pc < C::PCH; ++pc) {
-          const lds_u8* p = Vs + pc * 16 * C::ROW_BYTES + (db >> 1) * 128 +
-                            ((db & 1) ? v_off_odd : v_off_even);
-          typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+          const lds_u8* p = v_cur + pc * 16 * C::ROW_BYTES + (db / C::NVOFF) * 256 +
+                            v_off[db % C::NVOFF];
           const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
           const s16x4 hi =
               __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * C::ROW_BYTES));
@@ -316,16 +386,52 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_bf16_kernel(
               bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[pc], acc[db], 0, 0, 0);
         }
-    }
+      // ---- running sums: float32 weights and the bf16 weights P*V used ------
+      l_exact += rs;
+#pragma unroll
+      for (int pc = 0; pc < C::PCH; ++pc)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const bf16x2 two = {pf[pc][2 * t], pf[pc][2 * t + 1]};
+          l_round = __builtin_amdgcn_fdot2_f32_bf16(two, ones, l_round, false);
+        }
 
+      // Instruction order for the region: the S(j+1) MFMAs each followed by a
+      // share of the softmax VALU work, then the P*V MFMAs each with their
+      // transposed V reads and a share of the running sums; the operand reads
+      // run kLead MFMAs ahead of their use.
+      constexpr int kLead = 3;
+      __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);  // LDS read (K)
+#pragma unroll
+      for (int i = 0; i < C::KB * C::KCH; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kLead, 0);  // LDS read (V)
+#pragma unroll
+      for (int i = 0; i < C::DB * C::PCH; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS read
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
+      }
+    }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+  };
+  for (int j = 0; j < ntiles; j += 2) {
+    step(j, kbuf1, kbuf0, vbuf0, vbuf1, s_a, s_b);
+    if (j + 1 < ntiles) step(j + 1, kbuf0, kbuf1, vbuf1, vbuf0, s_b, s_a);
   }
 
-  if (!wave_active) return;
-  const float l_tot = l_part + other_half(l_part);
+  if (wave_ntiles == 0) return;
+  const float lr = l_round + swap_halves(l_round, hh);
+  const float le = l_exact + swap_halves(l_exact, hh);
   if (my_q >= S) return;
-  const float inv = 1.0f / l_tot;
+  // O is normalised by the sum of the bf16 weights that multiplied V, so the
+  // weights applied to V sum to one exactly (up to float32 rounding); the
+  // log-sum-exp uses the float32 weights.
+  const float inv = 1.0f / lr;
   uint16_t* Orow = O + head + (size_t)my_q * D;
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
@@ -342,7 +448,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_bf16_kernel(
       }
       *reinterpret_cast<u32x2*>(Orow + db * 32 + gq * 8 + hh * 4) = pk;
     }
-  if (hh == 0) LSE[(size_t)bh * S + my_q] = (m_run * c + fast_log2(l_tot)) * kLn2;
+  if (hh == 0) LSE[(size_t)bh * S + my_q] = (m_run * c + fast_log2(le)) * kLn2;
 }
 
 // ----------------------------------------------------------------------------
@@ -493,10 +599,8 @@ bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
 }
 
 struct Plan {
-  int nq;
   int bh_total;
   int group_heads;
-  unsigned grid;
   float c;
 };
 
@@ -508,8 +612,9 @@ int validate(const void* q, const void* k, const void* v, const void* o, const f
   if (causal != 0 && causal != 1) return FA_ERR_CAUSAL;
   if (!(scale > 0.0f) || !isfinite(scale)) return FA_ERR_SCALE;
   const int64_t bh = (int64_t)B * H;
-  const int64_t nq = ((int64_t)S + kBr - 1) / kBr;
-  if (bh > INT32_MAX || (int64_t)S * D > INT32_MAX || nq * bh > INT32_MAX) return FA_ERR_SHAPE;
+  // every configuration uses query tiles of at least 128 rows
+  const int64_t nq_max = ((int64_t)S + 127) / 128;
+  if (bh > INT32_MAX || (int64_t)S * D > INT32_MAX || nq_max * bh > INT32_MAX) return FA_ERR_SHAPE;
   const int64_t n = bh * S * D;
   if ((uint64_t)n > (uint64_t)(SIZE_MAX / elem) / 2) return FA_ERR_SHAPE;
   const uintptr_t a16 = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o;
@@ -520,19 +625,17 @@ int validate(const void* q, const void* k, const void* v, const void* o, const f
       ranges_overlap(lse, lb, k, tb) || ranges_overlap(lse, lb, v, tb) ||
       ranges_overlap(lse, lb, o, tb))
     return FA_ERR_ALIAS;
-  plan->nq = (int)nq;
   plan->bh_total = (int)bh;
   plan->group_heads = bh >= 8 ? (int)(bh / 8) : 1;
-  plan->grid = (unsigned)(nq * bh);
   plan->c = scale * kLog2e;
   return FA_OK;
 }
 
 template <class KernelT, class... Args>
-int launch(KernelT kernel, const Plan& p, hipStream_t stream, Args... args) {
+int launch(KernelT kernel, unsigned grid, unsigned threads, hipStream_t stream, Args... args) {
   void* argv[] = {static_cast<void*>(&args)...};
-  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(p.grid),
-                                       dim3(kThreads), argv, 0, stream);
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(grid),
+                                       dim3(threads), argv, 0, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -543,21 +646,25 @@ int run_bf16(const void* q, const void* k, const void* v, void* o, float* lse, i
   const uint16_t* K = static_cast<const uint16_t*>(k);
   const uint16_t* V = static_cast<const uint16_t*>(v);
   uint16_t* Out = static_cast<uint16_t*>(o);
+  const int nq = (S + kBr - 1) / kBr;
+  const unsigned grid = (unsigned)nq * (unsigned)p.bh_total;
   if (causal)
-    return launch(fa_fwd_bf16_kernel<D, BC, true>, p, stream, Q, K, V, Out, lse, S, p.nq,
-                  p.bh_total, p.group_heads, p.c);
-  return launch(fa_fwd_bf16_kernel<D, BC, false>, p, stream, Q, K, V, Out, lse, S, p.nq,
-                p.bh_total, p.group_heads, p.c);
+    return launch(fa_fwd_bf16_kernel<D, BC, true>, grid, kThreads, stream, Q, K, V, Out, lse, S,
+                  nq, p.bh_total, p.group_heads, p.c);
+  return launch(fa_fwd_bf16_kernel<D, BC, false>, grid, kThreads, stream, Q, K, V, Out, lse, S,
+                nq, p.bh_total, p.group_heads, p.c);
 }
 
 template <int D>
 int run_f32(const float* q, const float* k, const float* v, float* o, float* lse, int S,
             bool causal, const Plan& p, hipStream_t stream) {
+  const int nq = (S + kBr - 1) / kBr;
+  const unsigned grid = (unsigned)nq * (unsigned)p.bh_total;
   if (causal)
-    return launch(fa_fwd_f32_kernel<D, true>, p, stream, q, k, v, o, lse, S, p.nq, p.bh_total,
-                  p.group_heads, p.c);
-  return launch(fa_fwd_f32_kernel<D, false>, p, stream, q, k, v, o, lse, S, p.nq, p.bh_total,
-                p.group_heads, p.c);
+    return launch(fa_fwd_f32_kernel<D, true>, grid, kThreads, stream, q, k, v, o, lse, S, nq,
+                  p.bh_total, p.group_heads, p.c);
+  return launch(fa_fwd_f32_kernel<D, false>, grid, kThreads, stream, q, k, v, o, lse, S, nq,
+                p.bh_total, p.group_heads, p.c);
 }
 
 }  // namespace
