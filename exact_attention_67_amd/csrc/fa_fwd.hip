@@ -221,6 +221,17 @@ __device__ __forceinline__ void qk_tile(f32x16 (&s)[C::KB], const lds_u8* Ks,
   }
 }
 
+// Row max of a tile's raw scores for the lane's query (both lane halves).
+template <class C>
+__device__ __forceinline__ float row_max(const f32x16 (&s)[C::KB], int hh) {
+  float x = s[0][0];
+#pragma unroll
+  for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x = fmaxf(x, s[kb][r]);
+  return fmaxf(x, swap_halves(x, hh));
+}
+
 // Two waves per SIMD up to D = 128; D = 256 needs the full register file.
 template <int D, int BC, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void fa_fwd_bf16_kernel(
@@ -315,18 +326,25 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void fa_fwd_bf16_kernel
   __syncthreads();
   // S tiles in two named buffers used alternately (no copy between tiles).
   f32x16 s_a[C::KB], s_b[C::KB];
-  if (wave_ntiles > 0) qk_tile<C>(s_a, kbuf0, qf, k_off);
+  float mt_a = 0.0f, mt_b = 0.0f;  // row max of s_a / s_b
+  if (wave_ntiles > 0) {
+    qk_tile<C>(s_a, kbuf0, qf, k_off);
+    mt_a = row_max<C>(s_a, hh);
+  }
   __syncthreads();  // every wave is done with K(0) before K(2) overwrites it
 
   // Iteration j: start K(j+2) and V(j+1); compute S(j+1) into s_out while the
   // weights of tile j (s_in) form; then O += P(j) V(j).
   auto step = [&](const int j, lds_u8* k_next, lds_u8* k_load, const lds_u8* v_cur,
-                  lds_u8* v_load, f32x16 (&s_in)[C::KB], f32x16 (&s_out)[C::KB]) {
+                  lds_u8* v_load, f32x16 (&s_in)[C::KB], f32x16 (&s_out)[C::KB],
+                  float& mt_in, float& mt_out) {
     if (j + 2 < ntiles) issue_tile<C>(Kh, k_load, (j + 2) * BC, S, wave, koff, krow);
     if (j + 1 < ntiles) issue_tile<C>(Vh, v_load, (j + 1) * BC, S, wave, voff, vrow);
     if (j < wave_ntiles) {
       const int k0 = j * BC;
-      // ---- mask (diagonal and tail tiles only) -----------------------------
+      // ---- mask (diagonal and tail tiles only) and the tile's row max -------
+      // (for unmasked tiles the max was taken during the previous tile)
+      float mt = mt_in;
       if ((CAUSAL && (k0 + BC - 1 > qw0)) || (k0 + BC > S)) {
         const int lim = (CAUSAL ? min(my_q, S - 1) : (S - 1)) - k0 - hh * 8;
 #pragma unroll
@@ -336,14 +354,9 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void fa_fwd_bf16_kernel
             const int key = kb * 32 + (r >> 3) * 16 + (r & 7);
             s_in[kb][r] = key > lim ? -INFINITY : s_in[kb][r];
           }
+        mt = row_max<C>(s_in, hh);
       }
-      // ---- tile max; the (rare) move of the reference max ------------------
-      float mt = s_in[0][0];
-#pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s_in[kb][r]);
-      mt = fmaxf(mt, swap_halves(mt, hh));
+      // ---- the (rare) move of the reference max ------------------------------
       // true on the first tile (m_run = -inf); every row has an unmasked key
       // in tile 0, so no NaN arises here
       if (__any((mt - m_run) * c > kRescaleThreshold)) {
@@ -373,10 +386,12 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void fa_fwd_bf16_kernel
         }
 
       // ---- O^T += V^T * P^T -------------------------------------------------
+      // Key-chunk-major: the chunks of the first 32 keys only need the first
+      // half of the weights, so the second half's exponentials overlap them.
 #pragma unroll
-      for (int db = 0; db < C::DB; ++db)
+      for (int pc = 0; pc < C::PCH; ++pc)
 #pragma unroll
-        for (int pc = 0; pc < C::PCH; ++pc) {
+        for (int db = 0; db < C::DB; ++db) {
           const lds_u8* p = v_cur + pc * 16 * C::ROW_BYTES + (db / C::NVOFF) * 256 +
                             v_off[db % C::NVOFF];
           const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
@@ -395,33 +410,35 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void fa_fwd_bf16_kernel
           const bf16x2 two = {pf[pc][2 * t], pf[pc][2 * t + 1]};
           l_round = __builtin_amdgcn_fdot2_f32_bf16(two, ones, l_round, false);
         }
+      // ---- row max of S(j+1) for the next tile ------------------------------
+      mt_out = row_max<C>(s_out, hh);
 
-      // Instruction order for the region: the S(j+1) MFMAs each followed by a
-      // share of the softmax VALU work, then the P*V MFMAs each with their
-      // transposed V reads and a share of the running sums; the operand reads
-      // run kLead MFMAs ahead of their use.
+      // Instruction order for the region: every MFMA (S(j+1), then P*V) is
+      // followed by its share of the VALU work (exponentials, conversions, row
+      // sums, the next tile's row max) and its operand reads, which run kLead
+      // MFMAs ahead of their use.
       constexpr int kLead = 3;
       __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);  // LDS read (K)
 #pragma unroll
       for (int i = 0; i < C::KB * C::KCH; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
       }
       __builtin_amdgcn_sched_group_barrier(0x100, 2 * kLead, 0);  // LDS read (V)
 #pragma unroll
       for (int i = 0; i < C::DB * C::PCH; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS read
-        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
       }
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
   for (int j = 0; j < ntiles; j += 2) {
-    step(j, kbuf1, kbuf0, vbuf0, vbuf1, s_a, s_b);
-    if (j + 1 < ntiles) step(j + 1, kbuf0, kbuf1, vbuf1, vbuf0, s_b, s_a);
+    step(j, kbuf1, kbuf0, vbuf0, vbuf1, s_a, s_b, mt_a, mt_b);
+    if (j + 1 < ntiles) step(j + 1, kbuf0, kbuf1, vbuf1, vbuf0, s_b, s_a, mt_b, mt_a);
   }
 
   if (wave_ntiles == 0) return;
