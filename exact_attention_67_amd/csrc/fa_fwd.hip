@@ -185,7 +185,12 @@ template <class C>
 __device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ head_src, lds_u8* dst,
                                            int k0, int S, int wave, const int* off,
                                            const int* row) {
-  const char* base = (const char*)(head_src + (size_t)k0 * C::D);
+  // The tile's base address is wave-uniform: keep it in scalar registers so
+  // each copy is issued as scalar base + 32-bit lane offset.
+  const uint64_t b64 = (uint64_t)(head_src + (size_t)k0 * C::D);
+  const uint32_t b_lo = __builtin_amdgcn_readfirstlane((uint32_t)b64);
+  const uint32_t b_hi = __builtin_amdgcn_readfirstlane((uint32_t)(b64 >> 32));
+  const char* base = (const char*)(((uint64_t)b_hi << 32) | b_lo);
   lds_u8* lds = dst + wave * (C::LOADS_PER_WAVE * 1024);
   if (k0 + C::BC <= S) {
 #pragma unroll
