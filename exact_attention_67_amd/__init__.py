@@ -28,11 +28,12 @@ from ._lib import (  # noqa: F401
     FAError,
     fa_fwd,
     fa_fwd_f32,
+    fa_fwd_plan,
     load,
     status_str,
 )
 
-__all__ = ["forward", "fa_fwd", "fa_fwd_f32", "load", "status_str", "FAError"]
+__all__ = ["forward", "fa_fwd", "fa_fwd_f32", "fa_fwd_plan", "load", "status_str", "FAError"]
 
 
 def forward(q, k, v, causal: bool = True, scale: Optional[float] = None,

@@ -26,7 +26,7 @@ FA_ERR_ALIGN = 6
 FA_ERR_ALIAS = 7
 FA_ERR_LAUNCH = 8
 
-EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_status_str", "fa_abi_version")
+EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_plan", "fa_status_str", "fa_abi_version")
 ABI_VERSION = 1
 
 _lock = threading.Lock()
@@ -48,6 +48,9 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.fa_fwd.restype = i
     lib.fa_fwd_f32.argtypes = sig
     lib.fa_fwd_f32.restype = i
+    ip = ctypes.POINTER(i)
+    lib.fa_fwd_plan.argtypes = [i, i, i, i, i, i, ip, ip, ip, ip]
+    lib.fa_fwd_plan.restype = i
     lib.fa_status_str.argtypes = [i]
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_abi_version.argtypes = []
@@ -88,3 +91,14 @@ def fa_fwd_f32(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, S: int,
                causal: int, scale: float, stream: int | None) -> int:
     """Raw C call on device addresses (ints).  Returns the fa_status."""
     return load().fa_fwd_f32(q, k, v, o, lse, B, H, S, D, causal, scale, stream)
+
+
+def fa_fwd_plan(B: int, H: int, S: int, D: int, causal: int, elem_bytes: int) -> dict:
+    """Launch shape the library uses for this problem (host-only query).
+    Returns {rows_per_group, keys_per_tile, threads, groups}; raises FAError."""
+    out = [ctypes.c_int(-1) for _ in range(4)]
+    st = load().fa_fwd_plan(B, H, S, D, causal, elem_bytes, *[ctypes.byref(x) for x in out])
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd_plan")
+    return dict(zip(("rows_per_group", "keys_per_tile", "threads", "groups"),
+                    (x.value for x in out)))

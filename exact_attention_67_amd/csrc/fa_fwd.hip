@@ -107,10 +107,12 @@ typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 // more than this many powers of two, so softmax weights stay <= 2^8.
 constexpr float kRescaleThreshold = 8.0f;
 
-template <int D_, int BC_>
+template <int D_, int BC_, int WAVES_>
 struct BfCfg {
   static constexpr int D = D_;
   static constexpr int BC = BC_;                       // keys per tile
+  static constexpr int WAVES = WAVES_;                 // wavefronts per workgroup
+  static constexpr int BR = kRowsPerWave * WAVES;      // query rows per workgroup
   static constexpr int KCH = D / 16;                   // MFMA k-steps of Q*K^T
   static constexpr int KB = BC / 32;                   // 32-key blocks per tile
   static constexpr int DB = D / 32;                    // 32-row blocks of O^T
@@ -120,13 +122,13 @@ struct BfCfg {
   static constexpr int LDS_BYTES = 4 * TILE_BYTES;     // 2 K + 2 V buffers
   static constexpr int RC = D / 8;                     // 16-byte chunks per row
   static constexpr int ROWS_PER_LOAD = 64 / RC;        // rows per 1 KiB wave load
-  static constexpr int LOADS_PER_WAVE = TILE_BYTES / 1024 / kWaves;  // per tensor
+  static constexpr int LOADS_PER_WAVE = TILE_BYTES / 1024 / WAVES;  // per tensor
   // LDS bank geometry: 64 banks of 4 bytes, i.e. 256-byte bank lines.
   static constexpr int ROWS_PER_LINE = 256 / ROW_BYTES > 1 ? 256 / ROW_BYTES : 1;
   static constexpr int CH_PER_LINE = 16;               // 16-byte chunks per bank line
   static constexpr int NKOFF = KCH < 8 ? KCH : 8;      // distinct K read offsets
   static constexpr int NVOFF = DB < 4 ? DB : 4;        // distinct V read offsets
-  static_assert(TILE_BYTES % (1024 * kWaves) == 0, "tile must split into 1 KiB wave loads");
+  static_assert(TILE_BYTES % (1024 * WAVES) == 0, "tile must split into 1 KiB wave loads");
   static_assert(D % 32 == 0 && BC % 32 == 0 && D >= 64 && RC <= 64, "tile shape");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
@@ -237,13 +239,14 @@ __device__ __forceinline__ float row_max(const f32x16 (&s)[C::KB], int hh) {
   return fmaxf(x, swap_halves(x, hh));
 }
 
-// Two waves per SIMD up to D = 128; D = 256 needs the full register file.
-template <int D, int BC, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void fa_fwd_bf16_kernel(
+// Two waves per SIMD up to D = 128 (two 4-wave or one 8-wave workgroup per
+// CU); D = 256 needs the full register file.
+template <int D, int BC, int WAVES, bool CAUSAL>
+__global__ __launch_bounds__(64 * WAVES, D <= 128 ? 2 : 1) void fa_fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
     int S, int nq, int bh_total, int group_heads, float c) {
-  using C = BfCfg<D, BC>;
+  using C = BfCfg<D, BC, WAVES>;
   // Four separate buffers (K and V, two each) rather than one array indexed
   // by tile parity: every access below names its buffer statically, so the
   // compiler can tell that an asynchronous copy into one buffer never aliases
@@ -271,12 +274,12 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void fa_fwd_bf16_kernel
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m = lane & 31;   // column of the 32x32 accumulator = query
   const int hh = lane >> 5;  // lane half
-  const int q0 = qt * kBr;
+  const int q0 = qt * C::BR;
   const int qw0 = q0 + wave * kRowsPerWave;
   const int my_q = qw0 + m;
 
   // Key tiles this workgroup visits, and how many of them this wave needs.
-  const int kend = CAUSAL ? min(S, q0 + kBr) : S;
+  const int kend = CAUSAL ? min(S, q0 + C::BR) : S;
   const int ntiles = (kend + BC - 1) / BC;
   const int wave_klast = CAUSAL ? min(qw0 + kRowsPerWave - 1, S - 1) : (S - 1);
   const int wave_ntiles = qw0 < S ? min(ntiles, wave_klast / BC + 1) : 0;
@@ -626,19 +629,28 @@ struct Plan {
   float c;
 };
 
-int validate(const void* q, const void* k, const void* v, const void* o, const float* lse,
-             int B, int H, int S, int D, int causal, float scale, size_t elem, Plan* plan) {
-  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+// Shape checks shared by the entry points and the plan query.
+int validate_shape(int B, int H, int S, int D, int causal, size_t elem) {
   if (B < 1 || H < 1 || S < 1) return FA_ERR_SHAPE;
   if (D != 64 && D != 128 && D != 256) return FA_ERR_HEADDIM;
   if (causal != 0 && causal != 1) return FA_ERR_CAUSAL;
-  if (!(scale > 0.0f) || !isfinite(scale)) return FA_ERR_SCALE;
   const int64_t bh = (int64_t)B * H;
   // every configuration uses query tiles of at least 128 rows
   const int64_t nq_max = ((int64_t)S + 127) / 128;
   if (bh > INT32_MAX || (int64_t)S * D > INT32_MAX || nq_max * bh > INT32_MAX) return FA_ERR_SHAPE;
   const int64_t n = bh * S * D;
   if ((uint64_t)n > (uint64_t)(SIZE_MAX / elem) / 2) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+int validate(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             int B, int H, int S, int D, int causal, float scale, size_t elem, Plan* plan) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  const int st = validate_shape(B, H, S, D, causal, elem);
+  if (st != FA_OK) return st;
+  if (!(scale > 0.0f) || !isfinite(scale)) return FA_ERR_SCALE;
+  const int64_t bh = (int64_t)B * H;
+  const int64_t n = bh * S * D;
   const uintptr_t a16 = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o;
   if ((a16 & 15u) || ((uintptr_t)lse & 3u)) return FA_ERR_ALIGN;
   const size_t tb = (size_t)n * elem, lb = (size_t)(bh * S) * sizeof(float);
@@ -661,20 +673,47 @@ int launch(KernelT kernel, unsigned grid, unsigned threads, hipStream_t stream, 
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
-template <int D, int BC>
+// Launch shape of the bf16 kernel for one call.
+struct LaunchCfg {
+  int waves;     // wavefronts per workgroup (32 query rows each)
+  int bc;        // keys per K/V tile
+  int nq;        // query tiles per head
+  unsigned grid; // workgroups
+};
+
+// Tile sizes: 64-key tiles up to D = 128, 32-key tiles at D = 256 (LDS and
+// registers).  Workgroup size: an 8-wave workgroup (256 query rows) shares
+// each staged K/V tile among twice as many rows as a 4-wave one, halving the
+// global->LDS copy volume per flop.  At D = 128 that pays when the grid still
+// holds enough workgroups to balance: one per CU without a mask, two per CU
+// with the causal mask, whose workgroups differ in length.  At D = 64 the
+// exponentials, not the copies, dominate, and D = 256 runs one wave per SIMD.
+LaunchCfg bf16_config(int S, int D, bool causal, int bh_total) {
+  constexpr int64_t kCUs = 256;
+  LaunchCfg cfg;
+  cfg.bc = D == 256 ? 32 : 64;
+  cfg.waves = 4;
+  if (D == 128 && (int64_t)((S + 255) / 256) * bh_total >= (causal ? 2 : 1) * kCUs)
+    cfg.waves = 8;
+  const int br = kRowsPerWave * cfg.waves;
+  cfg.nq = (S + br - 1) / br;
+  cfg.grid = (unsigned)cfg.nq * (unsigned)bh_total;
+  return cfg;
+}
+
+template <int D, int BC, int WAVES>
 int run_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int S,
-             bool causal, const Plan& p, hipStream_t stream) {
+             bool causal, const Plan& p, const LaunchCfg& cfg, hipStream_t stream) {
+  static_assert(BfCfg<D, BC, WAVES>::BR == kRowsPerWave * WAVES, "rows per workgroup");
   const uint16_t* Q = static_cast<const uint16_t*>(q);
   const uint16_t* K = static_cast<const uint16_t*>(k);
   const uint16_t* V = static_cast<const uint16_t*>(v);
   uint16_t* Out = static_cast<uint16_t*>(o);
-  const int nq = (S + kBr - 1) / kBr;
-  const unsigned grid = (unsigned)nq * (unsigned)p.bh_total;
   if (causal)
-    return launch(fa_fwd_bf16_kernel<D, BC, true>, grid, kThreads, stream, Q, K, V, Out, lse, S,
-                  nq, p.bh_total, p.group_heads, p.c);
-  return launch(fa_fwd_bf16_kernel<D, BC, false>, grid, kThreads, stream, Q, K, V, Out, lse, S,
-                nq, p.bh_total, p.group_heads, p.c);
+    return launch(fa_fwd_bf16_kernel<D, BC, WAVES, true>, cfg.grid, 64 * WAVES, stream, Q, K, V,
+                  Out, lse, S, cfg.nq, p.bh_total, p.group_heads, p.c);
+  return launch(fa_fwd_bf16_kernel<D, BC, WAVES, false>, cfg.grid, 64 * WAVES, stream, Q, K, V,
+                Out, lse, S, cfg.nq, p.bh_total, p.group_heads, p.c);
 }
 
 template <int D>
@@ -697,10 +736,13 @@ extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, floa
   const int st = validate(q, k, v, o, lse, B, H, S, D, causal, scale, 2, &p);
   if (st != FA_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const LaunchCfg cfg = bf16_config(S, D, causal, p.bh_total);
   switch (D) {
-    case 64: return run_bf16<64, 64>(q, k, v, o, lse, S, causal, p, s);
-    case 128: return run_bf16<128, 64>(q, k, v, o, lse, S, causal, p, s);
-    default: return run_bf16<256, 32>(q, k, v, o, lse, S, causal, p, s);
+    case 64: return run_bf16<64, 64, 4>(q, k, v, o, lse, S, causal, p, cfg, s);
+    case 128:
+      if (cfg.waves == 8) return run_bf16<128, 64, 8>(q, k, v, o, lse, S, causal, p, cfg, s);
+      return run_bf16<128, 64, 4>(q, k, v, o, lse, S, causal, p, cfg, s);
+    default: return run_bf16<256, 32, 4>(q, k, v, o, lse, S, causal, p, cfg, s);
   }
 }
 
@@ -730,6 +772,32 @@ extern "C" const char* fa_status_str(int status) {
     case FA_ERR_LAUNCH: return "kernel launch failed";
     default: return "unknown status";
   }
+}
+
+extern "C" int fa_fwd_plan(int B, int H, int S, int D, int causal, int elem_bytes,
+                           int* rows_per_group, int* keys_per_tile, int* threads, int* groups) {
+  if (elem_bytes != 2 && elem_bytes != 4) return FA_ERR_SHAPE;
+  const int st = validate_shape(B, H, S, D, causal, (size_t)elem_bytes);
+  if (st != FA_OK) return st;
+  const int bh = B * H;
+  int rows, keys, thr, grid;
+  if (elem_bytes == 2) {
+    const LaunchCfg cfg = bf16_config(S, D, causal != 0, bh);
+    rows = kRowsPerWave * cfg.waves;
+    keys = cfg.bc;
+    thr = 64 * cfg.waves;
+    grid = (int)cfg.grid;
+  } else {
+    rows = kBr;
+    keys = F32Cfg<64>::BC;
+    thr = kThreads;
+    grid = ((S + kBr - 1) / kBr) * bh;
+  }
+  if (rows_per_group) *rows_per_group = rows;
+  if (keys_per_tile) *keys_per_tile = keys;
+  if (threads) *threads = thr;
+  if (groups) *groups = grid;
+  return FA_OK;
 }
 
 extern "C" int fa_abi_version(void) { return 1; }

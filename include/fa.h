@@ -88,6 +88,23 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                int B, int H, int S, int D, int causal, float scale, void* stream);
 
+/*
+ * fa_fwd_plan -- the launch shape fa_fwd (elem_bytes = 2) or fa_fwd_f32
+ * (elem_bytes = 4) uses for this problem, computed on the host without any
+ * HIP call (callable without a GPU).  One workgroup processes one tile of
+ * query rows of one (batch, head) -- the FlashAttention-2 blog's split of the
+ * work over sequence length ("FlashAttention-2 Optimizations", parallelism).
+ *   rows_per_group : query rows per workgroup
+ *   keys_per_tile  : keys per K/V tile staged in on-chip memory
+ *   threads        : threads per workgroup
+ *   groups         : workgroups in the grid
+ * Outputs are host pointers; each may be NULL.  Returns FA_ERR_SHAPE,
+ * FA_ERR_HEADDIM or FA_ERR_CAUSAL where fa_fwd would (FA_ERR_SHAPE also for
+ * elem_bytes other than 2 or 4), leaving the outputs untouched; else FA_OK.
+ */
+int fa_fwd_plan(int B, int H, int S, int D, int causal, int elem_bytes,
+                int* rows_per_group, int* keys_per_tile, int* threads, int* groups);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa_status_str(int status);
 

@@ -103,3 +103,47 @@ def test_forward_rejects_cpu_tensors():
 def test_missing_library_raises(tmp_path):
     with pytest.raises(RuntimeError):
         _lib.load(str(tmp_path / "nope.so"))
+
+
+# ---------------------------------------------------------------------------
+# The launch-shape query (host logic only)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("B,H,S,D,causal,eb", [
+    (1, 32, 16384, 128, 1, 2), (2, 16, 4096, 128, 1, 2), (2, 16, 4096, 128, 0, 2),
+    (1, 16, 4096, 128, 1, 2), (4, 16, 1024, 64, 1, 2), (2, 8, 8192, 256, 1, 2),
+    (1, 2, 128, 64, 1, 4), (3, 5, 1, 128, 0, 2), (7, 3, 257, 256, 0, 4), (32, 16, 300, 128, 1, 2)])
+def test_plan_covers_every_query_row(B, H, S, D, causal, eb):
+    p = fa.fa_fwd_plan(B, H, S, D, causal, eb)
+    rows, keys, thr, groups = (p["rows_per_group"], p["keys_per_tile"], p["threads"], p["groups"])
+    assert thr % 64 == 0 and rows == 32 * (thr // 64)       # 32 query rows per wavefront
+    assert keys in (32, 64)
+    assert groups % (B * H) == 0
+    per_head = groups // (B * H)
+    assert per_head * rows >= S > (per_head - 1) * rows     # every row once, no empty tile
+
+
+def test_plan_workgroup_choice():
+    # D = 128: 256-row workgroups once the grid still has >= 2 per CU (causal)
+    # or >= 1 per CU (no mask); 128-row workgroups otherwise and for D != 128.
+    assert fa.fa_fwd_plan(1, 32, 16384, 128, 1, 2)["rows_per_group"] == 256
+    assert fa.fa_fwd_plan(2, 16, 4096, 128, 1, 2)["rows_per_group"] == 256
+    assert fa.fa_fwd_plan(1, 16, 4096, 128, 1, 2)["rows_per_group"] == 128
+    assert fa.fa_fwd_plan(1, 16, 4096, 128, 0, 2)["rows_per_group"] == 256
+    assert fa.fa_fwd_plan(1, 8, 4096, 128, 0, 2)["rows_per_group"] == 128
+    assert fa.fa_fwd_plan(2, 16, 4096, 128, 0, 2)["rows_per_group"] == 256
+    assert fa.fa_fwd_plan(1, 32, 16384, 64, 1, 2)["rows_per_group"] == 128
+    assert fa.fa_fwd_plan(2, 8, 8192, 256, 1, 2) == dict(
+        rows_per_group=128, keys_per_tile=32, threads=256, groups=16 * 64)
+    assert fa.fa_fwd_plan(1, 32, 16384, 128, 1, 4) == dict(
+        rows_per_group=128, keys_per_tile=32, threads=256, groups=32 * 128)
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, 1, 128, 64, 1, 2), fa.FA_ERR_SHAPE), ((1, 1, 0, 64, 1, 2), fa.FA_ERR_SHAPE),
+    ((1, 1, 128, 96, 1, 2), fa.FA_ERR_HEADDIM), ((1, 1, 128, 64, 2, 2), fa.FA_ERR_CAUSAL),
+    ((1, 1, 128, 64, 1, 3), fa.FA_ERR_SHAPE), ((1 << 20, 1 << 12, 1 << 20, 64, 1, 2), fa.FA_ERR_SHAPE)])
+def test_plan_rejects_bad_shapes(args, status):
+    with pytest.raises(fa.FAError) as e:
+        fa.fa_fwd_plan(*args)
+    assert e.value.status == status

@@ -124,6 +124,36 @@ def test_other_scales(scale):
 
 
 # ---------------------------------------------------------------------------
+# Both bf16 workgroup shapes at D = 128 (4 waves = 128 query rows, 8 waves =
+# 256 rows; the library picks by grid size), with ragged last query tiles in
+# which some waves hold no rows at all
+# ---------------------------------------------------------------------------
+
+WG_CASES = [  # B, H, S, causal, rows per workgroup the library must pick
+    (32, 16, 300, True, 256),
+    (32, 16, 257, True, 256),
+    (16, 16, 300, False, 256),
+    (16, 16, 511, False, 256),
+    (1, 4, 300, True, 128),
+    (1, 4, 300, False, 128),
+]
+
+
+@pytest.mark.parametrize("B,H,S,causal,rows", WG_CASES,
+                         ids=[f"B{B}-H{H}-S{S}-{'c' if c else 'n'}-r{r}"
+                              for B, H, S, c, r in WG_CASES])
+def test_workgroup_shapes(B, H, S, causal, rows):
+    plan = fa.fa_fwd_plan(B, H, S, 128, int(causal), 2)
+    assert plan["rows_per_group"] == rows, plan
+    q, k, v = wl.make_qkv(B, H, S, 128, torch.bfloat16, seed=4000 + S + B)
+    scale = float(torch.tensor(1 / math.sqrt(128), dtype=torch.float32))
+    o, lse = run(q, k, v, causal, scale)
+    o_ref, l_ref = orc.attention_reference(q, k, v, causal, scale)
+    check(o, lse, o_ref, l_ref, torch.bfloat16,
+          f"workgroup rows={rows} B={B} H={H} S={S} causal={causal}")
+
+
+# ---------------------------------------------------------------------------
 # Closed forms on the GPU path
 # ---------------------------------------------------------------------------
 
