@@ -122,13 +122,19 @@ struct BfCfg {
   static constexpr int LDS_BYTES = 4 * TILE_BYTES;     // 2 K + 2 V buffers
   static constexpr int RC = D / 8;                     // 16-byte chunks per row
   static constexpr int ROWS_PER_LOAD = 64 / RC;        // rows per 1 KiB wave load
-  static constexpr int LOADS_PER_WAVE = TILE_BYTES / 1024 / WAVES;  // per tensor
+  // Waves that issue the tile copies: all of a 4-wave workgroup; in an 8-wave
+  // workgroup only waves 0..3 (one per SIMD), which leaves their SIMD
+  // partners free to start on the matrix cores right after the barrier.
+  static constexpr int COPY_WAVES = WAVES == 8 ? 4 : WAVES;
+  static constexpr int LOADS_PER_WAVE = TILE_BYTES / 1024 / COPY_WAVES;  // per tensor
+  // VALU instructions the schedule places after each MFMA of a tile.
+  static constexpr int VALU_PER_MFMA = WAVES == 8 ? 4 : 5;
   // LDS bank geometry: 64 banks of 4 bytes, i.e. 256-byte bank lines.
   static constexpr int ROWS_PER_LINE = 256 / ROW_BYTES > 1 ? 256 / ROW_BYTES : 1;
   static constexpr int CH_PER_LINE = 16;               // 16-byte chunks per bank line
   static constexpr int NKOFF = KCH < 8 ? KCH : 8;      // distinct K read offsets
   static constexpr int NVOFF = DB < 4 ? DB : 4;        // distinct V read offsets
-  static_assert(TILE_BYTES % (1024 * WAVES) == 0, "tile must split into 1 KiB wave loads");
+  static_assert(TILE_BYTES % (1024 * COPY_WAVES) == 0, "tile must split into 1 KiB wave loads");
   static_assert(D % 32 == 0 && BC % 32 == 0 && D >= 64 && RC <= 64, "tile shape");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
@@ -167,10 +173,10 @@ __device__ __forceinline__ float swap_halves(float x, int hh) {
 // 16-byte pieces this lane copies; row r of the tile lands in LDS row r with
 // its chunks swizzled.
 template <class C, bool IS_V>
-__device__ __forceinline__ void tile_offsets(int* off, int* row, int wave, int lane) {
+__device__ __forceinline__ void tile_offsets(int* off, int* row, int part, int lane) {
 #pragma unroll
   for (int u = 0; u < C::LOADS_PER_WAVE; ++u) {
-    const int n = wave * C::LOADS_PER_WAVE + u;
+    const int n = part * C::LOADS_PER_WAVE + u;
     const int r = n * C::ROWS_PER_LOAD + lane / C::RC;
     const int lch = (lane % C::RC) ^ (IS_V ? vswz<C>(r) : kswz<C>(r));
     row[u] = r;
@@ -178,14 +184,14 @@ __device__ __forceinline__ void tile_offsets(int* off, int* row, int wave, int l
   }
 }
 
-// Asynchronous global -> LDS copy of one K or V tile: this wave issues
-// LOADS_PER_WAVE transfers of 1 KiB, lane l filling bytes 16l .. 16l+15 (a
-// wave-uniform base address plus a per-lane 32-bit offset).  In the last
-// (partial) tile, rows past the sequence end are clamped to the last row:
-// finite data whose keys are masked.
+// Asynchronous global -> LDS copy of one K or V tile.  Share `part` of the
+// copy, issued by one wave, is LOADS_PER_WAVE transfers of 1 KiB, lane l
+// filling bytes 16l .. 16l+15 (a wave-uniform base address plus a per-lane
+// 32-bit offset).  In the last (partial) tile, rows past the sequence end are
+// clamped to the last row: finite data whose keys are masked.
 template <class C>
 __device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ head_src, lds_u8* dst,
-                                           int k0, int S, int wave, const int* off,
+                                           int k0, int S, int part, const int* off,
                                            const int* row) {
   // The tile's base address is wave-uniform: keep it in scalar registers so
   // each copy is issued as scalar base + 32-bit lane offset.
@@ -193,7 +199,7 @@ __device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ head_src
   const uint32_t b_lo = __builtin_amdgcn_readfirstlane((uint32_t)b64);
   const uint32_t b_hi = __builtin_amdgcn_readfirstlane((uint32_t)(b64 >> 32));
   const char* base = (const char*)(((uint64_t)b_hi << 32) | b_lo);
-  lds_u8* lds = dst + wave * (C::LOADS_PER_WAVE * 1024);
+  lds_u8* lds = dst + part * (C::LOADS_PER_WAVE * 1024);
   if (k0 + C::BC <= S) {
 #pragma unroll
     for (int u = 0; u < C::LOADS_PER_WAVE; ++u) {
@@ -286,13 +292,17 @@ __global__ __launch_bounds__(64 * WAVES, D <= 128 ? 2 : 1) void fa_fwd_bf16_kern
 
   int koff[C::LOADS_PER_WAVE], krow[C::LOADS_PER_WAVE];
   int voff[C::LOADS_PER_WAVE], vrow[C::LOADS_PER_WAVE];
-  tile_offsets<C, false>(koff, krow, wave, lane);
-  tile_offsets<C, true>(voff, vrow, wave, lane);
+  const bool copier = wave < C::COPY_WAVES;
+  const int cw = copier ? wave : 0;  // this wave's share of each tile copy
+  tile_offsets<C, false>(koff, krow, cw, lane);
+  tile_offsets<C, true>(voff, vrow, cw, lane);
 
   // The K stream runs one tile ahead of the V stream: K(0), K(1), V(0) now.
-  issue_tile<C>(Kh, kbuf0, 0, S, wave, koff, krow);
-  issue_tile<C>(Vh, vbuf0, 0, S, wave, voff, vrow);
-  if (ntiles > 1) issue_tile<C>(Kh, kbuf1, BC, S, wave, koff, krow);
+  if (copier) {
+    issue_tile<C>(Kh, kbuf0, 0, S, cw, koff, krow);
+    issue_tile<C>(Vh, vbuf0, 0, S, cw, voff, vrow);
+    if (ntiles > 1) issue_tile<C>(Kh, kbuf1, BC, S, cw, koff, krow);
+  }
 
   // Q fragments (B operand of S^T = K * Q^T): lane holds Q[my_q][ch*16 + hh*8 .. +8].
   bf16x8 qf[C::KCH];
@@ -346,8 +356,10 @@ __global__ __launch_bounds__(64 * WAVES, D <= 128 ? 2 : 1) void fa_fwd_bf16_kern
   auto step = [&](const int j, lds_u8* k_next, lds_u8* k_load, const lds_u8* v_cur,
                   lds_u8* v_load, f32x16 (&s_in)[C::KB], f32x16 (&s_out)[C::KB],
                   float& mt_in, float& mt_out) {
-    if (j + 2 < ntiles) issue_tile<C>(Kh, k_load, (j + 2) * BC, S, wave, koff, krow);
-    if (j + 1 < ntiles) issue_tile<C>(Vh, v_load, (j + 1) * BC, S, wave, voff, vrow);
+    if (copier) {
+      if (j + 2 < ntiles) issue_tile<C>(Kh, k_load, (j + 2) * BC, S, cw, koff, krow);
+      if (j + 1 < ntiles) issue_tile<C>(Vh, v_load, (j + 1) * BC, S, cw, voff, vrow);
+    }
     if (j < wave_ntiles) {
       const int k0 = j * BC;
       // ---- mask (diagonal and tail tiles only) and the tile's row max -------
@@ -431,14 +443,14 @@ __global__ __launch_bounds__(64 * WAVES, D <= 128 ? 2 : 1) void fa_fwd_bf16_kern
       for (int i = 0; i < C::KB * C::KCH; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
+        __builtin_amdgcn_sched_group_barrier(0x002, C::VALU_PER_MFMA, 0);  // VALU
       }
       __builtin_amdgcn_sched_group_barrier(0x100, 2 * kLead, 0);  // LDS read (V)
 #pragma unroll
       for (int i = 0; i < C::DB * C::PCH; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS read
-        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
+        __builtin_amdgcn_sched_group_barrier(0x002, C::VALU_PER_MFMA, 0);  // VALU
       }
     }
     __builtin_amdgcn_s_waitcnt(0);
