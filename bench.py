@@ -113,7 +113,8 @@ def time_workload(w, causal, steps, warmup):
 
 def cpu_baseline(w, causal, budget_s=20.0):
     """The oracle, as it stands, on the host cores over a bounded sample of the
-    same workload: whole heads (row-blocked), as many as fit the budget."""
+    same workload: whole heads (row-blocked), one after another until the time
+    budget is spent (or every head is done)."""
     import torch
     from oracle import attention as orc
     from tests import workloads as wl
@@ -130,7 +131,7 @@ def cpu_baseline(w, causal, budget_s=20.0):
         orc.attention_reference(q[sl], k[sl], v[sl], causal, w.scale, row_block=2048)
         t_total += time.perf_counter() - t
         done += 1
-        if t_total >= budget_s or done >= 8:
+        if t_total >= budget_s:
             break
     return {
         "value": flops_head * done / t_total / 1e12,

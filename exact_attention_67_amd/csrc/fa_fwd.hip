@@ -488,6 +488,321 @@ __global__ __launch_bounds__(64 * WAVES, D <= 128 ? 2 : 1) void fa_fwd_bf16_kern
   if (hh == 0) LSE[(size_t)bh * S + my_q] = (m_run * c + fast_log2(le)) * kLn2;
 }
 
+// Byte offsets (per lane) of the copies of the tile starting at key k0: in
+// the last (partial) tile, rows past the sequence end are clamped to the last
+// row (finite data whose keys are masked).
+template <class C>
+__device__ __forceinline__ void tile_src(const uint16_t* __restrict__ head_src, int k0, int S,
+                                         const int* off, const int* row, const char*& base,
+                                         int* boff) {
+  const uint64_t b64 = (uint64_t)(head_src + (size_t)k0 * C::D);
+  const uint32_t b_lo = __builtin_amdgcn_readfirstlane((uint32_t)b64);
+  const uint32_t b_hi = __builtin_amdgcn_readfirstlane((uint32_t)(b64 >> 32));
+  base = (const char*)(((uint64_t)b_hi << 32) | b_lo);
+  if (k0 + C::BC <= S) {
+#pragma unroll
+    for (int u = 0; u < C::LOADS_PER_WAVE; ++u) boff[u] = off[u] * 2;
+  } else {
+#pragma unroll
+    for (int u = 0; u < C::LOADS_PER_WAVE; ++u)
+      boff[u] = (off[u] - (row[u] - min(row[u], S - 1 - k0)) * C::D) * 2;
+  }
+}
+
+// One 1 KiB piece (16 bytes per lane) of a tile copy into LDS.
+__device__ __forceinline__ void copy_piece(const char* base, int boff, lds_u8* dst) {
+  const void* gp = base + (uint32_t)boff;
+  __builtin_amdgcn_global_load_lds(gp, dst, 16, 0, 0);
+}
+
+// A workgroup barrier that waits for nothing by itself (copies in flight stay
+// in flight); no instruction moves across it.
+__device__ __forceinline__ void plain_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// s_waitcnt immediate: at most n vector-memory operations outstanding, all
+// LDS operations done (expcnt untouched).
+constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
+
+// ----------------------------------------------------------------------------
+// bf16 kernel with a four-deep K/V ring (used at D = 256)
+// ----------------------------------------------------------------------------
+// At D = 256 a wave needs the whole register file, so each SIMD runs a single
+// wave and nothing hides the start-of-tile copy issue or the wait for copies.
+// This variant keeps four K and four V buffers, issues each tile's copies in
+// the middle of the matrix-core work two tiles ahead of use, and at the end of
+// a tile waits only for the copies of the previous tile.  Same arithmetic,
+// tiling, masking and softmax as fa_fwd_bf16_kernel.
+template <int D, int BC, int WAVES, bool CAUSAL>
+__global__ __launch_bounds__(64 * WAVES, D <= 128 ? 2 : 1) void fa_fwd_bf16_ring_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
+    int S, int nq, int bh_total, int group_heads, float c) {
+  using C = BfCfg<D, BC, WAVES>;
+  constexpr int NL = C::LOADS_PER_WAVE;  // copy pieces per tensor per wave
+  // Rings of four K and four V buffers, each a separate array so that every
+  // access names its buffer statically.  Step j reads K(j+1) and V(j) and
+  // copies K(j+3) and V(j+2), each into the buffer whose last reader was step
+  // j-2; the copies of step j are waited for at the end of step j+1.
+  __shared__ __attribute__((aligned(1024))) uint8_t kb0_raw[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t kb1_raw[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t kb2_raw[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t kb3_raw[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vb0_raw[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vb1_raw[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vb2_raw[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vb3_raw[C::TILE_BYTES];
+  lds_u8* kb0 = (lds_u8*)kb0_raw;
+  lds_u8* kb1 = (lds_u8*)kb1_raw;
+  lds_u8* kb2 = (lds_u8*)kb2_raw;
+  lds_u8* kb3 = (lds_u8*)kb3_raw;
+  lds_u8* vb0 = (lds_u8*)vb0_raw;
+  lds_u8* vb1 = (lds_u8*)vb1_raw;
+  lds_u8* vb2 = (lds_u8*)vb2_raw;
+  lds_u8* vb3 = (lds_u8*)vb3_raw;
+
+  int bh, qt;
+  decode_tile<CAUSAL>(xcd_logical_index(blockIdx.x, nq * bh_total), nq, bh_total,
+                      group_heads, bh, qt);
+
+  const size_t head = (size_t)bh * (size_t)S * D;
+  const uint16_t* Qh = Q + head;
+  const uint16_t* Kh = K + head;
+  const uint16_t* Vh = V + head;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int m = lane & 31;
+  const int hh = lane >> 5;
+  const int q0 = qt * C::BR;
+  const int qw0 = q0 + wave * kRowsPerWave;
+  const int my_q = qw0 + m;
+
+  const int kend = CAUSAL ? min(S, q0 + C::BR) : S;
+  const int ntiles = (kend + BC - 1) / BC;
+  const int wave_klast = CAUSAL ? min(qw0 + kRowsPerWave - 1, S - 1) : (S - 1);
+  const int wave_ntiles = qw0 < S ? min(ntiles, wave_klast / BC + 1) : 0;
+
+  int koff[NL], krow[NL], voff[NL], vrow[NL];
+  tile_offsets<C, false>(koff, krow, wave, lane);
+  tile_offsets<C, true>(voff, vrow, wave, lane);
+  const int wslot = wave * (NL * 1024);  // this wave's share of a buffer
+
+  // Prologue copies: K(0..2), V(0..1) (tiles past the end: the last tile).
+  {
+    const char* b;
+    int bo[NL];
+    lds_u8* kdst[3] = {kb0, kb1, kb2};
+#pragma unroll
+    for (int t = 0; t < 3; ++t) {
+      tile_src<C>(Kh, min(t, ntiles - 1) * BC, S, koff, krow, b, bo);
+#pragma unroll
+      for (int u = 0; u < NL; ++u) copy_piece(b, bo[u], kdst[t] + wslot + u * 1024);
+    }
+    lds_u8* vdst[2] = {vb0, vb1};
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      tile_src<C>(Vh, min(t, ntiles - 1) * BC, S, voff, vrow, b, bo);
+#pragma unroll
+      for (int u = 0; u < NL; ++u) copy_piece(b, bo[u], vdst[t] + wslot + u * 1024);
+    }
+  }
+
+  bf16x8 qf[C::KCH];
+#pragma unroll
+  for (int ch = 0; ch < C::KCH; ++ch) {
+    u32x4 raw = u32x4{0u, 0u, 0u, 0u};
+    if (my_q < S) raw = *reinterpret_cast<const u32x4*>(Qh + (size_t)my_q * D + ch * 16 + hh * 8);
+    qf[ch] = __builtin_bit_cast(bf16x8, raw);
+  }
+
+  const int pm = key_perm(m);
+  const int ksw = kswz<C>(pm);
+  int k_off[C::NKOFF];
+#pragma unroll
+  for (int b = 0; b < C::NKOFF; ++b) k_off[b] = pm * C::ROW_BYTES + (((2 * b + hh) ^ ksw) << 4);
+  const int g = lane >> 4, j4 = (lane >> 2) & 3, t4 = lane & 3;
+  const int vx = 2 * (g & 1) + (t4 >> 1);
+  const int vsw = vswz<C>(hh * 8 + j4);
+  const int v_row = (hh * 8 + j4) * C::ROW_BYTES + (t4 & 1) * 8;
+  int v_off[C::NVOFF];
+#pragma unroll
+  for (int d4 = 0; d4 < C::NVOFF; ++d4) v_off[d4] = v_row + (((4 * d4 + vx) ^ vsw) << 4);
+
+  f32x16 acc[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
+  float m_run = -INFINITY;
+  float l_exact = 0.0f;
+  float l_round0 = 0.0f, l_round1 = 0.0f;  // two chains of the bf16-weight sum
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  f32x16 s_a[C::KB], s_b[C::KB];
+  float mt_a = 0.0f, mt_b = 0.0f;
+  if (wave_ntiles > 0) {
+    qk_tile<C>(s_a, kb0, qf, k_off);
+    mt_a = row_max<C>(s_a, hh);
+  }
+
+  auto step = [&](const int j, const lds_u8* k_next, lds_u8* k_load, const lds_u8* v_cur,
+                  lds_u8* v_load, f32x16 (&s_in)[C::KB], f32x16 (&s_out)[C::KB],
+                  float& mt_in, float& mt_out) {
+    // Sources of this step's copies (a valid tile even past the end, so that
+    // every step issues the same number of copies).
+    const char* kbase;
+    const char* vbase;
+    int kbo[NL], vbo[NL];
+    tile_src<C>(Kh, min(j + 3, ntiles - 1) * BC, S, koff, krow, kbase, kbo);
+    tile_src<C>(Vh, min(j + 2, ntiles - 1) * BC, S, voff, vrow, vbase, vbo);
+    lds_u8* kdst = k_load + wslot;
+    lds_u8* vdst = v_load + wslot;
+    if (j < wave_ntiles) {
+      const int k0 = j * BC;
+      float mt = mt_in;
+      if ((CAUSAL && (k0 + BC - 1 > qw0)) || (k0 + BC > S)) {
+        const int lim = (CAUSAL ? min(my_q, S - 1) : (S - 1)) - k0 - hh * 8;
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kb * 32 + (r >> 3) * 16 + (r & 7);
+            s_in[kb][r] = key > lim ? -INFINITY : s_in[kb][r];
+          }
+        mt = row_max<C>(s_in, hh);
+      }
+      if (__any((mt - m_run) * c > kRescaleThreshold)) {
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha = fast_exp2((m_run - m_new) * c);
+        m_run = m_new;
+        l_exact *= alpha;
+        l_round0 *= alpha;
+        l_round1 *= alpha;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) acc[db] *= alpha;
+      }
+      const float mc = m_run * c;
+
+      qk_tile<C>(s_out, k_next, qf, k_off);
+
+      float rs = 0.0f;
+      bf16x8 pf[C::PCH];
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = fast_exp2(fmaf(s_in[kb][r], c, -mc));
+          rs += p;
+          pf[2 * kb + (r >> 3)][r & 7] = (__bf16)p;
+        }
+
+#pragma unroll
+      for (int u = 0; u < NL; ++u) copy_piece(kbase, kbo[u], kdst + u * 1024);
+#pragma unroll
+      for (int u = 0; u < NL; ++u) copy_piece(vbase, vbo[u], vdst + u * 1024);
+
+#pragma unroll
+      for (int pc = 0; pc < C::PCH; ++pc)
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          const lds_u8* p = v_cur + pc * 16 * C::ROW_BYTES + (db / C::NVOFF) * 256 +
+                            v_off[db % C::NVOFF];
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+          const s16x4 hi =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * C::ROW_BYTES));
+          const bf16x8 vf = __builtin_bit_cast(
+              bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[pc], acc[db], 0, 0, 0);
+        }
+      l_exact += rs;
+#pragma unroll
+      for (int pc = 0; pc < C::PCH; ++pc)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const bf16x2 two = {pf[pc][2 * t], pf[pc][2 * t + 1]};
+          if (pc & 1) l_round1 = __builtin_amdgcn_fdot2_f32_bf16(two, ones, l_round1, false);
+          else l_round0 = __builtin_amdgcn_fdot2_f32_bf16(two, ones, l_round0, false);
+        }
+      mt_out = row_max<C>(s_out, hh);
+
+      // Instruction order: each MFMA is followed by its share of the vector
+      // work and of the operand reads (kLead MFMAs ahead); the copies spread
+      // over the region, one every 32 / (2 * NL) MFMAs.
+      constexpr int kLead = 3;
+      constexpr int kNM = C::KB * C::KCH + C::DB * C::PCH;  // MFMAs in the region
+      constexpr int kEvery = kNM / (2 * NL);
+      __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);
+#pragma unroll
+      for (int i = 0; i < C::KB * C::KCH; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+        if (i % kEvery == kEvery / 2) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kLead, 0);
+#pragma unroll
+      for (int i = 0; i < C::DB * C::PCH; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+        if (i % kEvery == kEvery / 2) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < NL; ++u) copy_piece(kbase, kbo[u], kdst + u * 1024);
+#pragma unroll
+      for (int u = 0; u < NL; ++u) copy_piece(vbase, vbo[u], vdst + u * 1024);
+    }
+    // The previous step's copies have landed (this step's stay in flight);
+    // this wave's LDS reads are done.
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * NL));
+    plain_barrier();
+  };
+  // Unrolled by four (ring position and S parity static); the remaining
+  // tiles run after the loop so that the back edge always follows step 3.
+  int j = 0;
+  for (; j + 3 < ntiles; j += 4) {
+    step(j, kb1, kb3, vb0, vb2, s_a, s_b, mt_a, mt_b);
+    step(j + 1, kb2, kb0, vb1, vb3, s_b, s_a, mt_b, mt_a);
+    step(j + 2, kb3, kb1, vb2, vb0, s_a, s_b, mt_a, mt_b);
+    step(j + 3, kb0, kb2, vb3, vb1, s_b, s_a, mt_b, mt_a);
+  }
+  if (j < ntiles) step(j, kb1, kb3, vb0, vb2, s_a, s_b, mt_a, mt_b);
+  if (j + 1 < ntiles) step(j + 1, kb2, kb0, vb1, vb3, s_b, s_a, mt_b, mt_a);
+  if (j + 2 < ntiles) step(j + 2, kb3, kb1, vb2, vb0, s_a, s_b, mt_a, mt_b);
+  __builtin_amdgcn_s_waitcnt(0);
+
+  if (wave_ntiles == 0) return;
+  const float l_round = l_round0 + l_round1;
+  const float lr = l_round + swap_halves(l_round, hh);
+  const float le = l_exact + swap_halves(l_exact, hh);
+  if (my_q >= S) return;
+  const float inv = 1.0f / lr;
+  uint16_t* Orow = O + head + (size_t)my_q * D;
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      u32x2 pk;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const __bf16 lo = (__bf16)(acc[db][gq * 4 + 2 * t] * inv);
+        const __bf16 hi = (__bf16)(acc[db][gq * 4 + 2 * t + 1] * inv);
+        pk[t] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+                ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+      }
+      *reinterpret_cast<u32x2*>(Orow + db * 32 + gq * 8 + hh * 4) = pk;
+    }
+  if (hh == 0) LSE[(size_t)bh * S + my_q] = (m_run * c + fast_log2(le)) * kLn2;
+}
+
 // ----------------------------------------------------------------------------
 // float32 kernel (v_mfma_f32_32x32x2_f32): same tiling and softmax, float32
 // operands and float32 softmax weights.  Single-buffered LDS, 32-key tiles.
@@ -721,11 +1036,19 @@ int run_bf16(const void* q, const void* k, const void* v, void* o, float* lse, i
   const uint16_t* K = static_cast<const uint16_t*>(k);
   const uint16_t* V = static_cast<const uint16_t*>(v);
   uint16_t* Out = static_cast<uint16_t*>(o);
-  if (causal)
-    return launch(fa_fwd_bf16_kernel<D, BC, WAVES, true>, cfg.grid, 64 * WAVES, stream, Q, K, V,
+  if constexpr (D == 256) {
+    if (causal)
+      return launch(fa_fwd_bf16_ring_kernel<D, BC, WAVES, true>, cfg.grid, 64 * WAVES, stream, Q,
+                    K, V, Out, lse, S, cfg.nq, p.bh_total, p.group_heads, p.c);
+    return launch(fa_fwd_bf16_ring_kernel<D, BC, WAVES, false>, cfg.grid, 64 * WAVES, stream, Q, K,
+                  V, Out, lse, S, cfg.nq, p.bh_total, p.group_heads, p.c);
+  } else {
+    if (causal)
+      return launch(fa_fwd_bf16_kernel<D, BC, WAVES, true>, cfg.grid, 64 * WAVES, stream, Q, K, V,
+                    Out, lse, S, cfg.nq, p.bh_total, p.group_heads, p.c);
+    return launch(fa_fwd_bf16_kernel<D, BC, WAVES, false>, cfg.grid, 64 * WAVES, stream, Q, K, V,
                   Out, lse, S, cfg.nq, p.bh_total, p.group_heads, p.c);
-  return launch(fa_fwd_bf16_kernel<D, BC, WAVES, false>, cfg.grid, 64 * WAVES, stream, Q, K, V,
-                Out, lse, S, cfg.nq, p.bh_total, p.group_heads, p.c);
+  }
 }
 
 template <int D>
