@@ -50,7 +50,7 @@ def recorded_traffic(workload: str):
         return None
     kv = {}
     for line in open(TRAFFIC_FILE):
-        m = re.match(r"^\s*([a-z_]+)\s*:\s*(\S+)", line)
+        m = re.match(r"^\s*([a-z0-9_]+)\s*:\s*(\S+)", line)
         if m:
             kv[m.group(1)] = m.group(2)
     if kv.get("source_sha256") != source_digest() or kv.get("workload") != workload:
