@@ -135,6 +135,8 @@ struct BfCfg {
   static constexpr int NKOFF = KCH < 8 ? KCH : 8;      // distinct K read offsets
   static constexpr int NVOFF = DB < 4 ? DB : 4;        // distinct V read offsets
   static_assert(TILE_BYTES % (1024 * COPY_WAVES) == 0, "tile must split into 1 KiB wave loads");
+  static_assert(COPY_WAVES * LOADS_PER_WAVE * 1024 == TILE_BYTES, "copy shares cover the tile");
+  static_assert(COPY_WAVES * LOADS_PER_WAVE * ROWS_PER_LOAD == BC, "copy rows stay in the tile");
   static_assert(D % 32 == 0 && BC % 32 == 0 && D >= 64 && RC <= 64, "tile shape");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
@@ -544,6 +546,9 @@ __global__ __launch_bounds__(64 * WAVES, D <= 128 ? 2 : 1) void fa_fwd_bf16_ring
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
     int S, int nq, int bh_total, int group_heads, float c) {
   using C = BfCfg<D, BC, WAVES>;
+  // Every wave copies its share (wave w fills bytes [w, w+1) * NL KiB of a
+  // buffer): the copy split must cover exactly the waves of the workgroup.
+  static_assert(C::COPY_WAVES == WAVES, "ring kernel: every wave issues tile copies");
   constexpr int NL = C::LOADS_PER_WAVE;  // copy pieces per tensor per wave
   // Rings of four K and four V buffers, each a separate array so that every
   // access names its buffer statically.  Step j reads K(j+1) and V(j) and
