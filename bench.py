@@ -32,6 +32,8 @@ PEAK_F32_TFLOPS = 157.3     # MI355X published fp32 matrix peak
 DEFAULT_WORKLOAD = "c4_bf16_causal_1x32x16384x128"
 SRC = os.path.join(ROOT, "exact_attention_67_amd", "csrc", "fa_fwd.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_bf16_c4_hbm_traffic.txt")
+NOMINAL_SCLK_MHZ = 2400.0   # clock of the published peak
+COLD_EVICT_BYTES = 512 << 20
 
 
 def log(*a):
@@ -43,9 +45,10 @@ def source_digest() -> str:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def recorded_traffic(workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if
-    it was taken on the current kernel source for this workload; else None."""
+def recorded_profile_value(workload: str, key: str):
+    """A figure from the committed rocprofv3 summary (HBM bytes per launch,
+    sustained shader clock), if it was taken on the current kernel source for
+    this workload; else None."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     kv = {}
@@ -56,12 +59,16 @@ def recorded_traffic(workload: str):
     if kv.get("source_sha256") != source_digest() or kv.get("workload") != workload:
         return None
     try:
-        return float(kv["traffic_bytes_per_launch"])
+        return float(kv[key])
     except (KeyError, ValueError):
         return None
 
 
-def time_workload(w, causal, steps, warmup):
+def recorded_traffic(workload: str):
+    return recorded_profile_value(workload, "traffic_bytes_per_launch")
+
+
+def time_workload(w, causal, steps, warmup, cold_launches=0):
     import torch
     import exact_attention_67_amd as fa
     from tests import workloads as wl
@@ -106,9 +113,26 @@ def time_workload(w, causal, steps, warmup):
         b.record(stream)
     torch.cuda.synchronize()
     per = sorted(a.elapsed_time(b) for a, b in evs)
-    return dict(total_ms=total_ms, wall_s=wall, ms_per_step=total_ms / steps,
-                launch_ms_avg=sum(per) / len(per), launch_ms_min=per[0],
-                launch_ms_med=per[len(per) // 2])
+    res = dict(total_ms=total_ms, wall_s=wall, ms_per_step=total_ms / steps,
+               launch_ms_avg=sum(per) / len(per), launch_ms_min=per[0],
+               launch_ms_med=per[len(per) // 2])
+
+    # Cold: before each timed launch (outside its event pair) write a 512 MiB
+    # buffer on the same stream, evicting L2 and the last-level cache.
+    if cold_launches > 0:
+        scratch = torch.empty(COLD_EVICT_BYTES, dtype=torch.uint8, device="cuda")
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(cold_launches)]
+        for i, (a, b) in enumerate(evs):
+            scratch.fill_(i & 0xFF)
+            a.record(stream)
+            step()
+            b.record(stream)
+        torch.cuda.synchronize()
+        cold = sorted(a.elapsed_time(b) for a, b in evs)
+        res.update(cold_ms_med=cold[len(cold) // 2], cold_ms_min=cold[0])
+        del scratch
+    return res
 
 
 def cpu_baseline(w, causal, budget_s=20.0):
@@ -193,13 +217,18 @@ def main():
     w = wl.WORKLOADS[a.workload]
     causal = (not a.noncausal) and (True in w.causal)
     log(f"[bench] {w.name} causal={causal} steps={a.steps} warmup={a.warmup}")
-    r = time_workload(w, causal, a.steps, a.warmup)
+    r = time_workload(w, causal, a.steps, a.warmup, cold_launches=min(20, a.steps))
     flops = w.flops(causal)
     value = flops / (r["ms_per_step"] * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == torch.bfloat16 else PEAK_F32_TFLOPS
     achieved = flops / (r["launch_ms_avg"] * 1e-3) / 1e12
     log(f"[bench] ms/step={r['ms_per_step']:.4f} launch avg={r['launch_ms_avg']:.4f} "
-        f"min={r['launch_ms_min']:.4f} -> {value:.1f} TFLOP/s ({100 * value / peak:.1f}% of peak)")
+        f"min={r['launch_ms_min']:.4f} med={r['launch_ms_med']:.4f} -> {value:.1f} TFLOP/s "
+        f"({100 * value / peak:.1f}% of peak); cold med={r['cold_ms_med']:.4f}")
+    cold_diff = 100.0 * (r["cold_ms_med"] - r["launch_ms_med"]) / r["launch_ms_med"]
+    if abs(cold_diff) > 5.0:
+        log(f"[bench] warm and cold launches differ by {cold_diff:.1f}%")
+    sclk = recorded_profile_value(w.name, "sclk_mhz_under_load")
 
     if a.all:
         log(f"{'workload':40s} {'mask':7s} {'ms':>9s} {'TFLOP/s':>9s} {'%peak':>6s}")
@@ -243,7 +272,20 @@ def main():
             "traffic": recorded_traffic(w.name),
             "kernel": "fa_fwd_bf16_kernel" if w.dtype == torch.bfloat16 else "fa_fwd_f32_kernel",
             "launch_ms_avg": round(r["launch_ms_avg"], 5),
+            "launch_ms_median": round(r["launch_ms_med"], 5),
+            "launch_ms_min": round(r["launch_ms_min"], 5),
             "flops_per_launch": flops,
+            # peak scaled to the shader clock this kernel sustained (rocprofv3
+            # counters over kernel time, committed summary), when available
+            "sclk_mhz_under_load": sclk,
+            "peak_at_sclk": round(peak * sclk / NOMINAL_SCLK_MHZ, 1) if sclk else None,
+            "frac_at_sclk": round(achieved / (peak * sclk / NOMINAL_SCLK_MHZ), 4) if sclk else None,
+        },
+        "cold": {
+            "evict_bytes": COLD_EVICT_BYTES,
+            "launch_ms_median": round(r["cold_ms_med"], 5),
+            "launch_ms_min": round(r["cold_ms_min"], 5),
+            "cold_vs_warm_pct": round(cold_diff, 2),
         },
         "cpu_baseline": cpu,
     }
