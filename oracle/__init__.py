@@ -9,3 +9,8 @@ from .attention import (  # noqa: F401
     causal_keep_mask,
     default_scale,
 )
+from .prefix import (  # noqa: F401
+    attention_prefix,
+    merge_reference,
+    prefix_keep_mask,
+)
