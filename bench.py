@@ -29,6 +29,7 @@ if ROOT not in sys.path:
 METRIC = "attention fwd TFLOPS (bf16, causal) and % of MI355X bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X published dense bf16 matrix peak
 PEAK_F32_TFLOPS = 157.3     # MI355X published fp32 matrix peak
+PEAK_HBM_GBS = 8000.0       # MI355X published HBM3E bandwidth
 DEFAULT_WORKLOAD = "c4_bf16_causal_1x32x16384x128"
 SRC = os.path.join(ROOT, "exact_attention_67_amd", "csrc", "fa_fwd.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_bf16_c4_hbm_traffic.txt")
@@ -135,6 +136,65 @@ def time_workload(w, causal, steps, warmup, cold_launches=0):
     return res
 
 
+def _time_launches(fn, steps, warmup):
+    """Mean, median and min of per-launch HIP event pairs on the current stream."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) for a, b in evs)
+    return sum(per) / len(per), per[len(per) // 2], per[0]
+
+
+def time_secondary(steps):
+    """The Sq != Sk path (chunked prefill, decode) and the merge over key sets,
+    each on its own synthetic workload; reported beside the headline figure."""
+    import torch
+    import exact_attention_67_amd as fa
+    from tests import workloads as wl
+
+    out = {}
+    for name, w in wl.PREFIX_WORKLOADS.items():
+        q, k, v = (t.cuda() for t in wl.make_prefix_inputs(w))
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.Sq), dtype=torch.float32, device="cuda")
+
+        def call():
+            fa.forward_kv(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+
+        avg, med, mn = _time_launches(call, steps, 3)
+        out[name] = {"launch_ms_avg": round(avg, 5), "launch_ms_median": round(med, 5),
+                     "tflops": round(w.flops() / (avg * 1e-3) / 1e12, 2),
+                     "kv_read_gbs": round(w.kv_bytes() / (avg * 1e-3) / 1e9, 1)}
+        log(f"[bench] {name}: {avg:.4f} ms, {out[name]['tflops']} TFLOP/s, "
+            f"K/V read {out[name]['kv_read_gbs']} GB/s")
+        del q, k, v, o, lse
+    for name, w in wl.MERGE_WORKLOADS.items():
+        op, lp = (t.cuda() for t in wl.make_merge_inputs(w))
+        o = torch.empty(op.shape[1:], dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty(lp.shape[1:], dtype=torch.float32, device="cuda")
+
+        def call():
+            fa.merge(op, lp, out=o, lse=lse)
+
+        avg, med, mn = _time_launches(call, steps, 3)
+        gbs = w.bytes_moved() / (avg * 1e-3) / 1e9
+        out[name] = {"launch_ms_avg": round(avg, 5), "launch_ms_median": round(med, 5),
+                     "bound": "hbm", "achieved_gbs": round(gbs, 1), "peak_gbs": PEAK_HBM_GBS,
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes_per_launch": w.bytes_moved()}
+        log(f"[bench] {name}: {avg:.4f} ms, {gbs:.0f} GB/s ({100 * gbs / PEAK_HBM_GBS:.1f}% of HBM)")
+        del op, lp, o, lse
+    return out
+
+
 def cpu_baseline(w, causal, budget_s=20.0):
     """The oracle, as it stands, on the host cores over a bounded sample of the
     same workload: whole heads (row-blocked), one after another until the time
@@ -192,6 +252,8 @@ def main():
     ap.add_argument("--noncausal", action="store_true", help="time the non-causal mask")
     ap.add_argument("--all", action="store_true", help="also time every workload (stderr)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the Sq != Sk and merge workloads")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     a = ap.parse_args()
@@ -241,6 +303,8 @@ def main():
                 log(f"{name:40s} {'causal' if c else 'full':7s} {rr['launch_ms_avg']:9.4f} "
                     f"{tf:9.1f} {100 * tf / pk:6.1f}")
 
+    secondary = None if a.no_secondary else time_secondary(max(5, a.steps // 5))
+
     cpu = None
     if rank == 0 and not a.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample ...")
@@ -288,6 +352,8 @@ def main():
             "cold_vs_warm_pct": round(cold_diff, 2),
         },
         "cpu_baseline": cpu,
+        # not part of `value`: the Sq != Sk path and the merge on their own workloads
+        "secondary": secondary,
     }
     if rank == 0:
         print(json.dumps(line), flush=True)

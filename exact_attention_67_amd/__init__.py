@@ -3,7 +3,9 @@
 ``forward(q, k, v, causal, scale)`` takes torch tensors of shape
 [B, H, S, D] on the GPU (bf16 or float32, contiguous), allocates O and LSE with
 torch, and calls the C ABI (``fa_fwd`` / ``fa_fwd_f32``) on torch's current
-stream.  torch only provides device memory and the stream; the computation is
+stream.  ``forward_kv`` is the bf16 call with Sq queries against Sk keys
+(``fa_fwd_kv``); ``merge`` combines results over disjoint key sets
+(``fa_merge``).  torch only provides device memory and the stream; the computation is
 entirely in the library's HIP kernels.
 """
 
@@ -28,12 +30,15 @@ from ._lib import (  # noqa: F401
     FAError,
     fa_fwd,
     fa_fwd_f32,
+    fa_fwd_kv,
     fa_fwd_plan,
+    fa_merge,
     load,
     status_str,
 )
 
-__all__ = ["forward", "fa_fwd", "fa_fwd_f32", "fa_fwd_plan", "load", "status_str", "FAError"]
+__all__ = ["forward", "forward_kv", "merge", "fa_fwd", "fa_fwd_f32", "fa_fwd_kv", "fa_merge",
+           "fa_fwd_plan", "load", "status_str", "FAError"]
 
 
 def forward(q, k, v, causal: bool = True, scale: Optional[float] = None,
@@ -74,4 +79,76 @@ def forward(q, k, v, causal: bool = True, scale: Optional[float] = None,
             B, H, S, D, int(bool(causal)), float(scale), s.cuda_stream)
     if st != FA_OK:
         raise FAError(st, fn.__name__)
+    return out, lse
+
+
+def _stream(stream, device):
+    import torch
+    return stream if stream is not None else torch.cuda.current_stream(device)
+
+
+def forward_kv(q, k, v, causal: bool = True, scale: Optional[float] = None,
+               out=None, lse=None, stream=None) -> Tuple[object, object]:
+    """bf16 attention of q [B,H,Sq,D] against k, v [B,H,Sk,D] (causal mask
+    aligned bottom-right: query i sees keys j <= i + Sk - Sq; rows with no
+    visible key give O = 0, LSE = -inf).  Returns (O [B,H,Sq,D], LSE [B,H,Sq])."""
+    import torch
+
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k, v must be GPU tensors")
+    if not (q.dtype == k.dtype == v.dtype == torch.bfloat16):
+        raise ValueError("forward_kv takes bf16 q, k, v")
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape:
+        raise ValueError("q must be [B,H,Sq,D] and k, v one [B,H,Sk,D] shape")
+    B, H, Sq, D = (int(x) for x in q.shape)
+    if (int(k.shape[0]), int(k.shape[1]), int(k.shape[3])) != (B, H, D):
+        raise ValueError("q and k, v must agree on B, H and D")
+    Sk = int(k.shape[2])
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    if out.dtype != q.dtype or tuple(out.shape) != (B, H, Sq, D) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 [B,H,Sq,D] tensor")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Sq) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B,H,Sq] tensor")
+    s = _stream(stream, q.device)
+    st = fa_fwd_kv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                   B, H, Sq, Sk, D, int(bool(causal)), float(scale), s.cuda_stream)
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd_kv")
+    return out, lse
+
+
+def merge(o_parts, lse_parts, out=None, lse=None, stream=None) -> Tuple[object, object]:
+    """Merge G results over disjoint key sets: o_parts bf16 [G,B,H,S,D],
+    lse_parts float32 [G,B,H,S] -> (O [B,H,S,D] bf16, LSE [B,H,S] float32)."""
+    import torch
+
+    if not (o_parts.is_cuda and lse_parts.is_cuda):
+        raise ValueError("o_parts and lse_parts must be GPU tensors")
+    if o_parts.dtype != torch.bfloat16 or lse_parts.dtype != torch.float32:
+        raise ValueError("o_parts must be bf16 and lse_parts float32")
+    if o_parts.dim() != 5 or tuple(lse_parts.shape) != tuple(o_parts.shape[:4]):
+        raise ValueError("o_parts must be [G,B,H,S,D] and lse_parts [G,B,H,S]")
+    if not (o_parts.is_contiguous() and lse_parts.is_contiguous()):
+        raise ValueError("o_parts and lse_parts must be contiguous")
+    G, B, H, S, D = (int(x) for x in o_parts.shape)
+    if out is None:
+        out = torch.empty((B, H, S, D), dtype=torch.bfloat16, device=o_parts.device)
+    if lse is None:
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=o_parts.device)
+    if out.dtype != torch.bfloat16 or tuple(out.shape) != (B, H, S, D) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 [B,H,S,D] tensor")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, S) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B,H,S] tensor")
+    s = _stream(stream, o_parts.device)
+    st = fa_merge(o_parts.data_ptr(), lse_parts.data_ptr(), G, B, H, S, D, out.data_ptr(),
+                  lse.data_ptr(), s.cuda_stream)
+    if st != FA_OK:
+        raise FAError(st, "fa_merge")
     return out, lse

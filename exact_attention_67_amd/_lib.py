@@ -26,7 +26,8 @@ FA_ERR_ALIGN = 6
 FA_ERR_ALIAS = 7
 FA_ERR_LAUNCH = 8
 
-EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_plan", "fa_status_str", "fa_abi_version")
+EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_kv", "fa_merge", "fa_fwd_plan", "fa_status_str",
+           "fa_abi_version")
 ABI_VERSION = 1
 
 _lock = threading.Lock()
@@ -48,6 +49,10 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.fa_fwd.restype = i
     lib.fa_fwd_f32.argtypes = sig
     lib.fa_fwd_f32.restype = i
+    lib.fa_fwd_kv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+    lib.fa_fwd_kv.restype = i
+    lib.fa_merge.argtypes = [vp, vp, i, i, i, i, i, vp, vp, vp]
+    lib.fa_merge.restype = i
     ip = ctypes.POINTER(i)
     lib.fa_fwd_plan.argtypes = [i, i, i, i, i, i, ip, ip, ip, ip]
     lib.fa_fwd_plan.restype = i
@@ -91,6 +96,18 @@ def fa_fwd_f32(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, S: int,
                causal: int, scale: float, stream: int | None) -> int:
     """Raw C call on device addresses (ints).  Returns the fa_status."""
     return load().fa_fwd_f32(q, k, v, o, lse, B, H, S, D, causal, scale, stream)
+
+
+def fa_fwd_kv(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, Sq: int, Sk: int,
+              D: int, causal: int, scale: float, stream: int | None) -> int:
+    """Raw C call on device addresses (ints).  Returns the fa_status."""
+    return load().fa_fwd_kv(q, k, v, o, lse, B, H, Sq, Sk, D, causal, scale, stream)
+
+
+def fa_merge(o_parts: int, lse_parts: int, G: int, B: int, H: int, S: int, D: int, o: int,
+             lse: int, stream: int | None) -> int:
+    """Raw C call on device addresses (ints).  Returns the fa_status."""
+    return load().fa_merge(o_parts, lse_parts, G, B, H, S, D, o, lse, stream)
 
 
 def fa_fwd_plan(B: int, H: int, S: int, D: int, causal: int, elem_bytes: int) -> dict:

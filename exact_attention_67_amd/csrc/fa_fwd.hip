@@ -253,7 +253,7 @@ template <int D, int BC, int WAVES, bool CAUSAL>
 __global__ __launch_bounds__(64 * WAVES, D <= 128 ? 2 : 1) void fa_fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
-    int S, int nq, int bh_total, int group_heads, float c) {
+    int Sq, int Sk, int nq, int bh_total, int group_heads, float c) {
   using C = BfCfg<D, BC, WAVES>;
   // Four separate buffers (K and V, two each) rather than one array indexed
   // by tile parity: every access below names its buffer statically, so the
@@ -272,10 +272,11 @@ __global__ __launch_bounds__(64 * WAVES, D <= 128 ? 2 : 1) void fa_fwd_bf16_kern
   decode_tile<CAUSAL>(xcd_logical_index(blockIdx.x, nq * bh_total), nq, bh_total,
                       group_heads, bh, qt);
 
-  const size_t head = (size_t)bh * (size_t)S * D;
-  const uint16_t* Qh = Q + head;
-  const uint16_t* Kh = K + head;
-  const uint16_t* Vh = V + head;
+  const size_t qhead = (size_t)bh * (size_t)Sq * D;  // q and o of this head
+  const size_t khead = (size_t)bh * (size_t)Sk * D;  // k and v of this head
+  const uint16_t* Qh = Q + qhead;
+  const uint16_t* Kh = K + khead;
+  const uint16_t* Vh = V + khead;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -287,10 +288,15 @@ __global__ __launch_bounds__(64 * WAVES, D <= 128 ? 2 : 1) void fa_fwd_bf16_kern
   const int my_q = qw0 + m;
 
   // Key tiles this workgroup visits, and how many of them this wave needs.
-  const int kend = CAUSAL ? min(S, q0 + C::BR) : S;
+  // The queries are the last Sq positions of the Sk keys' sequence: with the
+  // causal mask, query row i sees keys j <= i + kshift (bottom-right
+  // alignment; kshift = 0 for self-attention).  Rows before the first key see
+  // nothing (possible when Sq > Sk).
+  const int kshift = Sk - Sq;
+  const int kend = CAUSAL ? max(0, min(Sk, q0 + C::BR + kshift)) : Sk;
   const int ntiles = (kend + BC - 1) / BC;
-  const int wave_klast = CAUSAL ? min(qw0 + kRowsPerWave - 1, S - 1) : (S - 1);
-  const int wave_ntiles = qw0 < S ? min(ntiles, wave_klast / BC + 1) : 0;
+  const int wave_klast = CAUSAL ? min(qw0 + kRowsPerWave - 1 + kshift, Sk - 1) : (Sk - 1);
+  const int wave_ntiles = (qw0 < Sq && wave_klast >= 0) ? min(ntiles, wave_klast / BC + 1) : 0;
 
   int koff[C::LOADS_PER_WAVE], krow[C::LOADS_PER_WAVE];
   int voff[C::LOADS_PER_WAVE], vrow[C::LOADS_PER_WAVE];
@@ -300,10 +306,10 @@ __global__ __launch_bounds__(64 * WAVES, D <= 128 ? 2 : 1) void fa_fwd_bf16_kern
   tile_offsets<C, true>(voff, vrow, cw, lane);
 
   // The K stream runs one tile ahead of the V stream: K(0), K(1), V(0) now.
-  if (copier) {
-    issue_tile<C>(Kh, kbuf0, 0, S, cw, koff, krow);
-    issue_tile<C>(Vh, vbuf0, 0, S, cw, voff, vrow);
-    if (ntiles > 1) issue_tile<C>(Kh, kbuf1, BC, S, cw, koff, krow);
+  if (copier && ntiles > 0) {
+    issue_tile<C>(Kh, kbuf0, 0, Sk, cw, koff, krow);
+    issue_tile<C>(Vh, vbuf0, 0, Sk, cw, voff, vrow);
+    if (ntiles > 1) issue_tile<C>(Kh, kbuf1, BC, Sk, cw, koff, krow);
   }
 
   // Q fragments (B operand of S^T = K * Q^T): lane holds Q[my_q][ch*16 + hh*8 .. +8].
@@ -311,7 +317,7 @@ __global__ __launch_bounds__(64 * WAVES, D <= 128 ? 2 : 1) void fa_fwd_bf16_kern
 #pragma unroll
   for (int ch = 0; ch < C::KCH; ++ch) {
     u32x4 raw = u32x4{0u, 0u, 0u, 0u};
-    if (my_q < S) raw = *reinterpret_cast<const u32x4*>(Qh + (size_t)my_q * D + ch * 16 + hh * 8);
+    if (my_q < Sq) raw = *reinterpret_cast<const u32x4*>(Qh + (size_t)my_q * D + ch * 16 + hh * 8);
     qf[ch] = __builtin_bit_cast(bf16x8, raw);
   }
 
@@ -359,16 +365,16 @@ __global__ __launch_bounds__(64 * WAVES, D <= 128 ? 2 : 1) void fa_fwd_bf16_kern
                   lds_u8* v_load, f32x16 (&s_in)[C::KB], f32x16 (&s_out)[C::KB],
                   float& mt_in, float& mt_out) {
     if (copier) {
-      if (j + 2 < ntiles) issue_tile<C>(Kh, k_load, (j + 2) * BC, S, cw, koff, krow);
-      if (j + 1 < ntiles) issue_tile<C>(Vh, v_load, (j + 1) * BC, S, cw, voff, vrow);
+      if (j + 2 < ntiles) issue_tile<C>(Kh, k_load, (j + 2) * BC, Sk, cw, koff, krow);
+      if (j + 1 < ntiles) issue_tile<C>(Vh, v_load, (j + 1) * BC, Sk, cw, voff, vrow);
     }
     if (j < wave_ntiles) {
       const int k0 = j * BC;
       // ---- mask (diagonal and tail tiles only) and the tile's row max -------
       // (for unmasked tiles the max was taken during the previous tile)
       float mt = mt_in;
-      if ((CAUSAL && (k0 + BC - 1 > qw0)) || (k0 + BC > S)) {
-        const int lim = (CAUSAL ? min(my_q, S - 1) : (S - 1)) - k0 - hh * 8;
+      if ((CAUSAL && (k0 + BC - 1 > qw0 + kshift)) || (k0 + BC > Sk)) {
+        const int lim = (CAUSAL ? min(my_q + kshift, Sk - 1) : (Sk - 1)) - k0 - hh * 8;
 #pragma unroll
         for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
@@ -379,18 +385,24 @@ __global__ __launch_bounds__(64 * WAVES, D <= 128 ? 2 : 1) void fa_fwd_bf16_kern
         mt = row_max<C>(s_in, hh);
       }
       // ---- the (rare) move of the reference max ------------------------------
-      // true on the first tile (m_run = -inf); every row has an unmasked key
-      // in tile 0, so no NaN arises here
+      // true on the first tile with a visible key for some row (m_run = -inf
+      // there); for a row with no visible key yet, -inf - -inf is NaN and the
+      // comparison is false
       if (__any((mt - m_run) * c > kRescaleThreshold)) {
         const float m_new = fmaxf(m_run, mt);
-        const float alpha = fast_exp2((m_run - m_new) * c);  // 0 on the first tile
+        // 0 when the row's first keys arrive; 1 for rows whose reference
+        // does not move (also rows that have seen no key yet: -inf, -inf)
+        const float alpha = m_new == m_run ? 1.0f : fast_exp2((m_run - m_new) * c);
         m_run = m_new;
         l_exact *= alpha;
         l_round *= alpha;
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) acc[db] *= alpha;
       }
-      const float mc = m_run * c;
+      // A row whose reference is still -inf has only masked keys in this tile
+      // (a finite one would have moved the reference above): its weights are
+      // exp2(-inf - 0) = 0.
+      const float mc = m_run == -INFINITY ? 0.0f : m_run * c;
 
       // ---- S(j+1) on the matrix cores (result unused past the last tile) ---
       qk_tile<C>(s_out, k_next, qf, k_off);
@@ -463,15 +475,14 @@ __global__ __launch_bounds__(64 * WAVES, D <= 128 ? 2 : 1) void fa_fwd_bf16_kern
     if (j + 1 < ntiles) step(j + 1, kbuf0, kbuf1, vbuf1, vbuf0, s_b, s_a, mt_b, mt_a);
   }
 
-  if (wave_ntiles == 0) return;
   const float lr = l_round + swap_halves(l_round, hh);
   const float le = l_exact + swap_halves(l_exact, hh);
-  if (my_q >= S) return;
+  if (my_q >= Sq) return;
   // O is normalised by the sum of the bf16 weights that multiplied V, so the
   // weights applied to V sum to one exactly (up to float32 rounding); the
   // log-sum-exp uses the float32 weights.
-  const float inv = 1.0f / lr;
-  uint16_t* Orow = O + head + (size_t)my_q * D;
+  const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
+  uint16_t* Orow = O + qhead + (size_t)my_q * D;
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
 #pragma unroll
@@ -487,7 +498,8 @@ __global__ __launch_bounds__(64 * WAVES, D <= 128 ? 2 : 1) void fa_fwd_bf16_kern
       }
       *reinterpret_cast<u32x2*>(Orow + db * 32 + gq * 8 + hh * 4) = pk;
     }
-  if (hh == 0) LSE[(size_t)bh * S + my_q] = (m_run * c + fast_log2(le)) * kLn2;
+  // A row that saw no key keeps m_run = -inf and le = 0: O = 0, LSE = -inf.
+  if (hh == 0) LSE[(size_t)bh * Sq + my_q] = (m_run * c + fast_log2(le)) * kLn2;
 }
 
 // Byte offsets (per lane) of the copies of the tile starting at key k0: in
@@ -544,7 +556,7 @@ template <int D, int BC, int WAVES, bool CAUSAL>
 __global__ __launch_bounds__(64 * WAVES, D <= 128 ? 2 : 1) void fa_fwd_bf16_ring_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
-    int S, int nq, int bh_total, int group_heads, float c) {
+    int Sq, int Sk, int nq, int bh_total, int group_heads, float c) {
   using C = BfCfg<D, BC, WAVES>;
   // Every wave copies its share (wave w fills bytes [w, w+1) * NL KiB of a
   // buffer): the copy split must cover exactly the waves of the workgroup.
@@ -575,10 +587,11 @@ __global__ __launch_bounds__(64 * WAVES, D <= 128 ? 2 : 1) void fa_fwd_bf16_ring
   decode_tile<CAUSAL>(xcd_logical_index(blockIdx.x, nq * bh_total), nq, bh_total,
                       group_heads, bh, qt);
 
-  const size_t head = (size_t)bh * (size_t)S * D;
-  const uint16_t* Qh = Q + head;
-  const uint16_t* Kh = K + head;
-  const uint16_t* Vh = V + head;
+  const size_t qhead = (size_t)bh * (size_t)Sq * D;  // q and o of this head
+  const size_t khead = (size_t)bh * (size_t)Sk * D;  // k and v of this head
+  const uint16_t* Qh = Q + qhead;
+  const uint16_t* Kh = K + khead;
+  const uint16_t* Vh = V + khead;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -589,10 +602,15 @@ __global__ __launch_bounds__(64 * WAVES, D <= 128 ? 2 : 1) void fa_fwd_bf16_ring
   const int qw0 = q0 + wave * kRowsPerWave;
   const int my_q = qw0 + m;
 
-  const int kend = CAUSAL ? min(S, q0 + C::BR) : S;
+  // The queries are the last Sq positions of the Sk keys' sequence: with the
+  // causal mask, query row i sees keys j <= i + kshift (bottom-right
+  // alignment; kshift = 0 for self-attention).  Rows before the first key see
+  // nothing (possible when Sq > Sk).
+  const int kshift = Sk - Sq;
+  const int kend = CAUSAL ? max(0, min(Sk, q0 + C::BR + kshift)) : Sk;
   const int ntiles = (kend + BC - 1) / BC;
-  const int wave_klast = CAUSAL ? min(qw0 + kRowsPerWave - 1, S - 1) : (S - 1);
-  const int wave_ntiles = qw0 < S ? min(ntiles, wave_klast / BC + 1) : 0;
+  const int wave_klast = CAUSAL ? min(qw0 + kRowsPerWave - 1 + kshift, Sk - 1) : (Sk - 1);
+  const int wave_ntiles = (qw0 < Sq && wave_klast >= 0) ? min(ntiles, wave_klast / BC + 1) : 0;
 
   int koff[NL], krow[NL], voff[NL], vrow[NL];
   tile_offsets<C, false>(koff, krow, wave, lane);
@@ -600,20 +618,20 @@ __global__ __launch_bounds__(64 * WAVES, D <= 128 ? 2 : 1) void fa_fwd_bf16_ring
   const int wslot = wave * (NL * 1024);  // this wave's share of a buffer
 
   // Prologue copies: K(0..2), V(0..1) (tiles past the end: the last tile).
-  {
+  if (ntiles > 0) {
     const char* b;
     int bo[NL];
     lds_u8* kdst[3] = {kb0, kb1, kb2};
 #pragma unroll
     for (int t = 0; t < 3; ++t) {
-      tile_src<C>(Kh, min(t, ntiles - 1) * BC, S, koff, krow, b, bo);
+      tile_src<C>(Kh, min(t, ntiles - 1) * BC, Sk, koff, krow, b, bo);
 #pragma unroll
       for (int u = 0; u < NL; ++u) copy_piece(b, bo[u], kdst[t] + wslot + u * 1024);
     }
     lds_u8* vdst[2] = {vb0, vb1};
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      tile_src<C>(Vh, min(t, ntiles - 1) * BC, S, voff, vrow, b, bo);
+      tile_src<C>(Vh, min(t, ntiles - 1) * BC, Sk, voff, vrow, b, bo);
 #pragma unroll
       for (int u = 0; u < NL; ++u) copy_piece(b, bo[u], vdst[t] + wslot + u * 1024);
     }
@@ -623,7 +641,7 @@ __global__ __launch_bounds__(64 * WAVES, D <= 128 ? 2 : 1) void fa_fwd_bf16_ring
 #pragma unroll
   for (int ch = 0; ch < C::KCH; ++ch) {
     u32x4 raw = u32x4{0u, 0u, 0u, 0u};
-    if (my_q < S) raw = *reinterpret_cast<const u32x4*>(Qh + (size_t)my_q * D + ch * 16 + hh * 8);
+    if (my_q < Sq) raw = *reinterpret_cast<const u32x4*>(Qh + (size_t)my_q * D + ch * 16 + hh * 8);
     qf[ch] = __builtin_bit_cast(bf16x8, raw);
   }
 
@@ -665,15 +683,15 @@ __global__ __launch_bounds__(64 * WAVES, D <= 128 ? 2 : 1) void fa_fwd_bf16_ring
     const char* kbase;
     const char* vbase;
     int kbo[NL], vbo[NL];
-    tile_src<C>(Kh, min(j + 3, ntiles - 1) * BC, S, koff, krow, kbase, kbo);
-    tile_src<C>(Vh, min(j + 2, ntiles - 1) * BC, S, voff, vrow, vbase, vbo);
+    tile_src<C>(Kh, min(j + 3, ntiles - 1) * BC, Sk, koff, krow, kbase, kbo);
+    tile_src<C>(Vh, min(j + 2, ntiles - 1) * BC, Sk, voff, vrow, vbase, vbo);
     lds_u8* kdst = k_load + wslot;
     lds_u8* vdst = v_load + wslot;
     if (j < wave_ntiles) {
       const int k0 = j * BC;
       float mt = mt_in;
-      if ((CAUSAL && (k0 + BC - 1 > qw0)) || (k0 + BC > S)) {
-        const int lim = (CAUSAL ? min(my_q, S - 1) : (S - 1)) - k0 - hh * 8;
+      if ((CAUSAL && (k0 + BC - 1 > qw0 + kshift)) || (k0 + BC > Sk)) {
+        const int lim = (CAUSAL ? min(my_q + kshift, Sk - 1) : (Sk - 1)) - k0 - hh * 8;
 #pragma unroll
         for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
@@ -685,7 +703,7 @@ __global__ __launch_bounds__(64 * WAVES, D <= 128 ? 2 : 1) void fa_fwd_bf16_ring
       }
       if (__any((mt - m_run) * c > kRescaleThreshold)) {
         const float m_new = fmaxf(m_run, mt);
-        const float alpha = fast_exp2((m_run - m_new) * c);
+        const float alpha = m_new == m_run ? 1.0f : fast_exp2((m_run - m_new) * c);
         m_run = m_new;
         l_exact *= alpha;
         l_round0 *= alpha;
@@ -693,7 +711,7 @@ __global__ __launch_bounds__(64 * WAVES, D <= 128 ? 2 : 1) void fa_fwd_bf16_ring
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) acc[db] *= alpha;
       }
-      const float mc = m_run * c;
+      const float mc = m_run == -INFINITY ? 0.0f : m_run * c;
 
       qk_tile<C>(s_out, k_next, qf, k_off);
 
@@ -784,13 +802,12 @@ __global__ __launch_bounds__(64 * WAVES, D <= 128 ? 2 : 1) void fa_fwd_bf16_ring
   if (j + 2 < ntiles) step(j + 2, kb3, kb1, vb2, vb0, s_a, s_b, mt_a, mt_b);
   __builtin_amdgcn_s_waitcnt(0);
 
-  if (wave_ntiles == 0) return;
   const float l_round = l_round0 + l_round1;
   const float lr = l_round + swap_halves(l_round, hh);
   const float le = l_exact + swap_halves(l_exact, hh);
-  if (my_q >= S) return;
-  const float inv = 1.0f / lr;
-  uint16_t* Orow = O + head + (size_t)my_q * D;
+  if (my_q >= Sq) return;
+  const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
+  uint16_t* Orow = O + qhead + (size_t)my_q * D;
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
 #pragma unroll
@@ -805,7 +822,8 @@ __global__ __launch_bounds__(64 * WAVES, D <= 128 ? 2 : 1) void fa_fwd_bf16_ring
       }
       *reinterpret_cast<u32x2*>(Orow + db * 32 + gq * 8 + hh * 4) = pk;
     }
-  if (hh == 0) LSE[(size_t)bh * S + my_q] = (m_run * c + fast_log2(le)) * kLn2;
+  // A row that saw no key keeps m_run = -inf and le = 0: O = 0, LSE = -inf.
+  if (hh == 0) LSE[(size_t)bh * Sq + my_q] = (m_run * c + fast_log2(le)) * kLn2;
 }
 
 // ----------------------------------------------------------------------------
@@ -961,35 +979,40 @@ struct Plan {
   float c;
 };
 
-// Shape checks shared by the entry points and the plan query.
-int validate_shape(int B, int H, int S, int D, int causal, size_t elem) {
-  if (B < 1 || H < 1 || S < 1) return FA_ERR_SHAPE;
+// Shape checks shared by the entry points and the plan query: Sq query rows
+// against Sk keys per (batch, head).
+int validate_shape(int B, int H, int Sq, int Sk, int D, int causal, size_t elem) {
+  if (B < 1 || H < 1 || Sq < 1 || Sk < 1) return FA_ERR_SHAPE;
   if (D != 64 && D != 128 && D != 256) return FA_ERR_HEADDIM;
   if (causal != 0 && causal != 1) return FA_ERR_CAUSAL;
   const int64_t bh = (int64_t)B * H;
   // every configuration uses query tiles of at least 128 rows
-  const int64_t nq_max = ((int64_t)S + 127) / 128;
-  if (bh > INT32_MAX || (int64_t)S * D > INT32_MAX || nq_max * bh > INT32_MAX) return FA_ERR_SHAPE;
-  const int64_t n = bh * S * D;
+  const int64_t nq_max = ((int64_t)Sq + 127) / 128;
+  if (bh > INT32_MAX || (int64_t)Sq * D > INT32_MAX || (int64_t)Sk * D > INT32_MAX ||
+      nq_max * bh > INT32_MAX)
+    return FA_ERR_SHAPE;
+  const int64_t n = bh * (int64_t)(Sq > Sk ? Sq : Sk) * D;
   if ((uint64_t)n > (uint64_t)(SIZE_MAX / elem) / 2) return FA_ERR_SHAPE;
   return FA_OK;
 }
 
 int validate(const void* q, const void* k, const void* v, const void* o, const float* lse,
-             int B, int H, int S, int D, int causal, float scale, size_t elem, Plan* plan) {
+             int B, int H, int Sq, int Sk, int D, int causal, float scale, size_t elem,
+             Plan* plan) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
-  const int st = validate_shape(B, H, S, D, causal, elem);
+  const int st = validate_shape(B, H, Sq, Sk, D, causal, elem);
   if (st != FA_OK) return st;
   if (!(scale > 0.0f) || !isfinite(scale)) return FA_ERR_SCALE;
   const int64_t bh = (int64_t)B * H;
-  const int64_t n = bh * S * D;
   const uintptr_t a16 = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o;
   if ((a16 & 15u) || ((uintptr_t)lse & 3u)) return FA_ERR_ALIGN;
-  const size_t tb = (size_t)n * elem, lb = (size_t)(bh * S) * sizeof(float);
-  if (ranges_overlap(o, tb, q, tb) || ranges_overlap(o, tb, k, tb) ||
-      ranges_overlap(o, tb, v, tb) || ranges_overlap(lse, lb, q, tb) ||
-      ranges_overlap(lse, lb, k, tb) || ranges_overlap(lse, lb, v, tb) ||
-      ranges_overlap(lse, lb, o, tb))
+  const size_t qb = (size_t)(bh * Sq * D) * elem;   // q and o
+  const size_t kb = (size_t)(bh * Sk * D) * elem;   // k and v
+  const size_t lb = (size_t)(bh * Sq) * sizeof(float);
+  if (ranges_overlap(o, qb, q, qb) || ranges_overlap(o, qb, k, kb) ||
+      ranges_overlap(o, qb, v, kb) || ranges_overlap(lse, lb, q, qb) ||
+      ranges_overlap(lse, lb, k, kb) || ranges_overlap(lse, lb, v, kb) ||
+      ranges_overlap(lse, lb, o, qb))
     return FA_ERR_ALIAS;
   plan->bh_total = (int)bh;
   plan->group_heads = bh >= 8 ? (int)(bh / 8) : 1;
@@ -1020,7 +1043,7 @@ struct LaunchCfg {
 // holds enough workgroups to balance: one per CU without a mask, two per CU
 // with the causal mask, whose workgroups differ in length.  At D = 64 the
 // exponentials, not the copies, dominate, and D = 256 runs one wave per SIMD.
-LaunchCfg bf16_config(int S, int D, bool causal, int bh_total) {
+LaunchCfg bf16_config(int S, int D, bool causal, int bh_total) {  // S: query rows
   constexpr int64_t kCUs = 256;
   LaunchCfg cfg;
   cfg.bc = D == 256 ? 32 : 64;
@@ -1034,7 +1057,7 @@ LaunchCfg bf16_config(int S, int D, bool causal, int bh_total) {
 }
 
 template <int D, int BC, int WAVES>
-int run_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int S,
+int run_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int Sq, int Sk,
              bool causal, const Plan& p, const LaunchCfg& cfg, hipStream_t stream) {
   static_assert(BfCfg<D, BC, WAVES>::BR == kRowsPerWave * WAVES, "rows per workgroup");
   const uint16_t* Q = static_cast<const uint16_t*>(q);
@@ -1044,15 +1067,15 @@ int run_bf16(const void* q, const void* k, const void* v, void* o, float* lse, i
   if constexpr (D == 256) {
     if (causal)
       return launch(fa_fwd_bf16_ring_kernel<D, BC, WAVES, true>, cfg.grid, 64 * WAVES, stream, Q,
-                    K, V, Out, lse, S, cfg.nq, p.bh_total, p.group_heads, p.c);
+                    K, V, Out, lse, Sq, Sk, cfg.nq, p.bh_total, p.group_heads, p.c);
     return launch(fa_fwd_bf16_ring_kernel<D, BC, WAVES, false>, cfg.grid, 64 * WAVES, stream, Q, K,
-                  V, Out, lse, S, cfg.nq, p.bh_total, p.group_heads, p.c);
+                  V, Out, lse, Sq, Sk, cfg.nq, p.bh_total, p.group_heads, p.c);
   } else {
     if (causal)
       return launch(fa_fwd_bf16_kernel<D, BC, WAVES, true>, cfg.grid, 64 * WAVES, stream, Q, K, V,
-                    Out, lse, S, cfg.nq, p.bh_total, p.group_heads, p.c);
+                    Out, lse, Sq, Sk, cfg.nq, p.bh_total, p.group_heads, p.c);
     return launch(fa_fwd_bf16_kernel<D, BC, WAVES, false>, cfg.grid, 64 * WAVES, stream, Q, K, V,
-                  Out, lse, S, cfg.nq, p.bh_total, p.group_heads, p.c);
+                  Out, lse, Sq, Sk, cfg.nq, p.bh_total, p.group_heads, p.c);
   }
 }
 
@@ -1068,28 +1091,112 @@ int run_f32(const float* q, const float* k, const float* v, float* o, float* lse
                 p.bh_total, p.group_heads, p.c);
 }
 
+int fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+             int Sq, int Sk, int D, int causal, float scale, void* stream) {
+  Plan p;
+  const int st = validate(q, k, v, o, lse, B, H, Sq, Sk, D, causal, scale, 2, &p);
+  if (st != FA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const LaunchCfg cfg = bf16_config(Sq, D, causal, p.bh_total);
+  switch (D) {
+    case 64: return run_bf16<64, 64, 4>(q, k, v, o, lse, Sq, Sk, causal, p, cfg, s);
+    case 128:
+      if (cfg.waves == 8) return run_bf16<128, 64, 8>(q, k, v, o, lse, Sq, Sk, causal, p, cfg, s);
+      return run_bf16<128, 64, 4>(q, k, v, o, lse, Sq, Sk, causal, p, cfg, s);
+    default: return run_bf16<256, 32, 4>(q, k, v, o, lse, Sq, Sk, causal, p, cfg, s);
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Merge of results computed over disjoint key sets
+// ----------------------------------------------------------------------------
+// LSE = log sum_g exp(LSE_g), O = sum_g exp(LSE_g - LSE) O_g, per output row.
+// One thread per 16 bytes (8 bf16) of an output row: 16-byte loads of each
+// part's O, float32 weights and sums, one bf16 (round to nearest even) store.
+// A part whose weight is 0 (LSE_g = -inf, or underflow) is skipped and its O
+// is not read.  A row with no visible key in any part: O = 0, LSE = -inf.
+template <int D>
+__global__ __launch_bounds__(256) void fa_merge_kernel(const uint16_t* __restrict__ Op,
+                                                       const float* __restrict__ Lp, int G,
+                                                       int64_t rows, uint16_t* __restrict__ O,
+                                                       float* __restrict__ L) {
+  constexpr int CPR = D / 8;  // 16-byte chunks per row
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= rows * CPR) return;
+  const int64_t r = t / CPR;
+  const int ch = (int)(t % CPR);
+  float m = -INFINITY;
+  for (int g = 0; g < G; ++g) m = fmaxf(m, Lp[g * rows + r]);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float lse = -INFINITY;
+  if (m != -INFINITY) {
+    float sum = 0.0f;
+    for (int g = 0; g < G; ++g) sum += fast_exp2((Lp[g * rows + r] - m) * kLog2e);
+    lse = m + fast_log2(sum) * kLn2;
+    for (int g = 0; g < G; ++g) {
+      const float w = fast_exp2((Lp[g * rows + r] - lse) * kLog2e);
+      if (w == 0.0f) continue;
+      const u32x4 raw = *reinterpret_cast<const u32x4*>(Op + (g * rows + r) * D + ch * 8);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += w * __builtin_bit_cast(float, raw[e] << 16);
+        acc[2 * e + 1] += w * __builtin_bit_cast(float, raw[e] & 0xFFFF0000u);
+      }
+    }
+  }
+  u32x4 out;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    out[e] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[2 * e]) |
+             ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[2 * e + 1]) << 16);
+  *reinterpret_cast<u32x4*>(O + r * D + ch * 8) = out;
+  if (ch == 0) L[r] = lse;
+}
+
 }  // namespace
 
 extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                       int H, int S, int D, int causal, float scale, void* stream) {
-  Plan p;
-  const int st = validate(q, k, v, o, lse, B, H, S, D, causal, scale, 2, &p);
-  if (st != FA_OK) return st;
+  return fwd_bf16(q, k, v, o, lse, B, H, S, S, D, causal, scale, stream);
+}
+
+extern "C" int fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                         int H, int Sq, int Sk, int D, int causal, float scale, void* stream) {
+  return fwd_bf16(q, k, v, o, lse, B, H, Sq, Sk, D, causal, scale, stream);
+}
+
+extern "C" int fa_merge(const void* o_parts, const float* lse_parts, int G, int B, int H, int S,
+                        int D, void* o, float* lse, void* stream) {
+  if (!o_parts || !lse_parts || !o || !lse) return FA_ERR_NULL;
+  if (G < 1 || B < 1 || H < 1 || S < 1) return FA_ERR_SHAPE;
+  if (D != 64 && D != 128 && D != 256) return FA_ERR_HEADDIM;
+  const int64_t rows = (int64_t)B * H * S;
+  if (rows > INT32_MAX || (uint64_t)G * (uint64_t)rows * D > (uint64_t)(SIZE_MAX / 4) ||
+      (uint64_t)(rows * (D / 8) + 255) / 256 > (uint64_t)UINT32_MAX)
+    return FA_ERR_SHAPE;
+  if ((((uintptr_t)o_parts | (uintptr_t)o) & 15u) ||
+      (((uintptr_t)lse_parts | (uintptr_t)lse) & 3u))
+    return FA_ERR_ALIGN;
+  const size_t ob = (size_t)rows * D * 2, lb = (size_t)rows * sizeof(float);
+  if (ranges_overlap(o, ob, o_parts, ob * G) || ranges_overlap(o, ob, lse_parts, lb * G) ||
+      ranges_overlap(lse, lb, o_parts, ob * G) || ranges_overlap(lse, lb, lse_parts, lb * G) ||
+      ranges_overlap(o, ob, lse, lb))
+    return FA_ERR_ALIAS;
+  const unsigned grid = (unsigned)((rows * (D / 8) + 255) / 256);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const LaunchCfg cfg = bf16_config(S, D, causal, p.bh_total);
+  const uint16_t* Op = static_cast<const uint16_t*>(o_parts);
+  uint16_t* Out = static_cast<uint16_t*>(o);
   switch (D) {
-    case 64: return run_bf16<64, 64, 4>(q, k, v, o, lse, S, causal, p, cfg, s);
-    case 128:
-      if (cfg.waves == 8) return run_bf16<128, 64, 8>(q, k, v, o, lse, S, causal, p, cfg, s);
-      return run_bf16<128, 64, 4>(q, k, v, o, lse, S, causal, p, cfg, s);
-    default: return run_bf16<256, 32, 4>(q, k, v, o, lse, S, causal, p, cfg, s);
+    case 64: return launch(fa_merge_kernel<64>, grid, 256, s, Op, lse_parts, G, rows, Out, lse);
+    case 128: return launch(fa_merge_kernel<128>, grid, 256, s, Op, lse_parts, G, rows, Out, lse);
+    default: return launch(fa_merge_kernel<256>, grid, 256, s, Op, lse_parts, G, rows, Out, lse);
   }
 }
 
 extern "C" int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                           int B, int H, int S, int D, int causal, float scale, void* stream) {
   Plan p;
-  const int st = validate(q, k, v, o, lse, B, H, S, D, causal, scale, 4, &p);
+  const int st = validate(q, k, v, o, lse, B, H, S, S, D, causal, scale, 4, &p);
   if (st != FA_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (D) {
@@ -1103,7 +1210,7 @@ extern "C" const char* fa_status_str(int status) {
   switch (status) {
     case FA_OK: return "ok";
     case FA_ERR_NULL: return "a tensor pointer is NULL";
-    case FA_ERR_SHAPE: return "B, H or S < 1, or a size overflows";
+    case FA_ERR_SHAPE: return "a size (B, H, S, Sq, Sk or G) is < 1, or a size overflows";
     case FA_ERR_HEADDIM: return "head dimension must be 64, 128 or 256";
     case FA_ERR_SCALE: return "scale must be finite and > 0";
     case FA_ERR_CAUSAL: return "causal must be 0 or 1";
@@ -1117,7 +1224,7 @@ extern "C" const char* fa_status_str(int status) {
 extern "C" int fa_fwd_plan(int B, int H, int S, int D, int causal, int elem_bytes,
                            int* rows_per_group, int* keys_per_tile, int* threads, int* groups) {
   if (elem_bytes != 2 && elem_bytes != 4) return FA_ERR_SHAPE;
-  const int st = validate_shape(B, H, S, D, causal, (size_t)elem_bytes);
+  const int st = validate_shape(B, H, S, S, D, causal, (size_t)elem_bytes);
   if (st != FA_OK) return st;
   const int bh = B * H;
   int rows, keys, thr, grid;

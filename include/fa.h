@@ -52,7 +52,7 @@ extern "C" {
 enum fa_status {
     FA_OK          = 0, /* enqueued */
     FA_ERR_NULL    = 1, /* a tensor pointer is NULL */
-    FA_ERR_SHAPE   = 2, /* B, H or S < 1, or a size/offset overflows */
+    FA_ERR_SHAPE   = 2, /* B, H, S (Sq, Sk, G) < 1, or a size/offset overflows */
     FA_ERR_HEADDIM = 3, /* D not one of 64, 128, 256 */
     FA_ERR_SCALE   = 4, /* scale not finite or not > 0 */
     FA_ERR_CAUSAL  = 5, /* causal not 0 or 1 */
@@ -89,6 +89,49 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
                int B, int H, int S, int D, int causal, float scale, void* stream);
 
 /*
+ * fa_fwd_kv -- bf16 attention of Sq queries against Sk keys (chunked prefill
+ * against a cached prefix, decode), with the causal mask aligned
+ * bottom-right.
+ *   q, o    : bf16 [B,H,Sq,D]; k, v : bf16 [B,H,Sk,D]; lse : float32 [B,H,Sq].
+ *   Sq, Sk  : query rows and keys per (batch, head), >= 1.
+ * The queries are taken to be the last Sq positions of the Sk-position
+ * sequence: with causal = 1, key j is visible to query i iff
+ * j <= i + (Sk - Sq).  This is the lower-triangular keep-matrix of
+ * "Profiling in PyTorch (Part 3): Attention is all you profile", section
+ * "Math backend", with its diagonal moved by Sk - Sq (the pages treat only
+ * Sq = Sk).  A row with no visible key (i < Sq - Sk) gets the result that
+ * section's safe softmax gives: o row = 0, lse = -inf.  With causal = 0
+ * every query sees all Sk keys.  fa_fwd(..., S, ...) is fa_fwd_kv with
+ * Sq = Sk = S.  Arithmetic, ownership, alignment and errors as for fa_fwd
+ * (FA_ERR_SHAPE also when Sq or Sk < 1).  The work is split over query
+ * tiles only, so a call with few query rows (decode) uses few workgroups.
+ */
+int fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse,
+              int B, int H, int Sq, int Sk, int D, int causal, float scale, void* stream);
+
+/*
+ * fa_merge -- combine G results computed over disjoint key sets of the same
+ * queries (split over keys: shards of a long key sequence, or a cached prefix
+ * and a new chunk) into the result over their union.
+ *   o_parts   : bf16 [G,B,H,S,D]   part g's output (device), e.g. from fa_fwd_kv.
+ *   lse_parts : float32 [G,B,H,S]  part g's natural-log LSE; -inf where a
+ *               row saw no key in that part.
+ *   o, lse    : bf16 [B,H,S,D] and float32 [B,H,S] results (device).
+ *   G >= 1 parts; D one of 64, 128, 256.
+ * Per row: lse = log sum_g exp(lse_g), o = sum_g exp(lse_g - lse) o_g,
+ * float32 weights and sums, o rounded to nearest even.  Parts whose weight is
+ * 0 (lse_g = -inf, or underflow) are skipped and their o is not read; a row
+ * with lse_g = -inf in every part gives o = 0, lse = -inf.  This identity
+ * follows from the definition of softmax over a union of key sets; it is the
+ * reason the per-row LSE is an output.  o_parts, o 16-byte aligned; lse_parts,
+ * lse 4-byte aligned; the outputs must not overlap the inputs or each other.
+ * Errors: FA_ERR_NULL, FA_ERR_SHAPE (G, B, H or S < 1, or a size overflows),
+ * FA_ERR_HEADDIM, FA_ERR_ALIGN, FA_ERR_ALIAS, FA_ERR_LAUNCH.
+ */
+int fa_merge(const void* o_parts, const float* lse_parts, int G, int B, int H, int S, int D,
+             void* o, float* lse, void* stream);
+
+/*
  * fa_fwd_plan -- the launch shape fa_fwd (elem_bytes = 2) or fa_fwd_f32
  * (elem_bytes = 4) uses for this problem, computed on the host without any
  * HIP call (callable without a GPU).  One workgroup processes one tile of
@@ -98,6 +141,7 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
  *   keys_per_tile  : keys per K/V tile staged in on-chip memory
  *   threads        : threads per workgroup
  *   groups         : workgroups in the grid
+ * For fa_fwd_kv pass S = Sq (the grid depends on the query rows only).
  * Outputs are host pointers; each may be NULL.  Returns FA_ERR_SHAPE,
  * FA_ERR_HEADDIM or FA_ERR_CAUSAL where fa_fwd would (FA_ERR_SHAPE also for
  * elem_bytes other than 2 or 4), leaving the outputs untouched; else FA_OK.

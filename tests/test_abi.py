@@ -93,6 +93,48 @@ def test_alias_rejected(f32):
     assert call(o=Q + n, causal=3, f32=f32) == fa.FA_ERR_CAUSAL
 
 
+def call_kv(q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, Sq=64, Sk=300, D=128, causal=1, scale=0.125):
+    return fa.fa_fwd_kv(q, k, v, o, lse, B, H, Sq, Sk, D, causal, scale, None)
+
+
+def test_fwd_kv_validation_errors():
+    for bad in ({"q": 0}, {"k": 0}, {"v": 0}, {"o": 0}, {"lse": 0}):
+        assert call_kv(**bad) == fa.FA_ERR_NULL, bad
+    for bad in ({"Sq": 0}, {"Sk": 0}, {"Sq": -3}, {"Sk": -1}, {"B": 0}):
+        assert call_kv(**bad) == fa.FA_ERR_SHAPE, bad
+    assert call_kv(D=96) == fa.FA_ERR_HEADDIM
+    assert call_kv(causal=2) == fa.FA_ERR_CAUSAL
+    assert call_kv(scale=math.nan) == fa.FA_ERR_SCALE
+    assert call_kv(k=K + 8) == fa.FA_ERR_ALIGN
+    assert call_kv(Sk=1 << 24, D=256) == fa.FA_ERR_SHAPE
+    # o is [B,H,Sq,D]; k is [B,H,Sk,D]: overlap computed with each one's size
+    kbytes = 1 * 2 * 300 * 128 * 2
+    qbytes = 1 * 2 * 64 * 128 * 2
+    assert call_kv(o=K + kbytes - 16) == fa.FA_ERR_ALIAS
+    assert call_kv(o=K + kbytes, causal=3) == fa.FA_ERR_CAUSAL     # adjacent: no alias
+    assert call_kv(lse=Q + qbytes - 4) == fa.FA_ERR_ALIAS
+    assert call_kv(lse=Q + qbytes, causal=3) == fa.FA_ERR_CAUSAL
+
+
+def call_merge(op=Q, lp=K, G=3, B=1, H=2, S=100, D=64, o=O, lse=L):
+    return fa.fa_merge(op, lp, G, B, H, S, D, o, lse, None)
+
+
+def test_merge_validation_errors():
+    for bad in ({"op": 0}, {"lp": 0}, {"o": 0}, {"lse": 0}):
+        assert call_merge(**bad) == fa.FA_ERR_NULL, bad
+    for bad in ({"G": 0}, {"B": 0}, {"H": -1}, {"S": 0}):
+        assert call_merge(**bad) == fa.FA_ERR_SHAPE, bad
+    assert call_merge(D=80) == fa.FA_ERR_HEADDIM
+    assert call_merge(op=Q + 8) == fa.FA_ERR_ALIGN
+    assert call_merge(lse=L + 2) == fa.FA_ERR_ALIGN
+    assert call_merge(B=1 << 16, H=1 << 12, S=1 << 10) == fa.FA_ERR_SHAPE
+    parts = 3 * 1 * 2 * 100 * 64 * 2
+    assert call_merge(o=Q + parts - 16) == fa.FA_ERR_ALIAS      # o inside the parts
+    assert call_merge(lse=K + 4) == fa.FA_ERR_ALIAS             # lse inside lse_parts
+    assert call_merge(o=O, lse=O + 64) == fa.FA_ERR_ALIAS       # outputs overlap
+
+
 def test_forward_rejects_cpu_tensors():
     import torch
     q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)

@@ -326,3 +326,12 @@ def test_merge_pins_catch_planted_mistakes(mutant):
         except (AssertionError, RuntimeError, ValueError):
             failed.append(pin.__name__)
     assert failed, f"no pin caught {mutant.__name__}"
+
+
+def test_workload_visible_pairs_match_the_mask():
+    from tests import workloads as wl
+    for sq, sk in ((1, 9), (5, 9), (9, 9), (12, 5), (7, 1)):
+        for causal in (False, True):
+            w = wl.PrefixWorkload("t", 1, 1, sq, sk, 64, causal, 0)
+            keep = pre.prefix_keep_mask(sq, sk) if causal else torch.ones(sq, sk, dtype=torch.bool)
+            assert w.visible_pairs() == int(keep.sum())

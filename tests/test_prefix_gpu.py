@@ -1,0 +1,203 @@
+"""GPU parity for queries against a key prefix (fa_fwd_kv) and for the merge
+of results over disjoint key sets (fa_merge), through the C ABI, against the
+float64 oracle (oracle/prefix.py).
+
+Tolerances are those of the square path: O max-abs error <= 2e-2, per-head
+relative RMS error <= 1e-2, LSE max-abs error <= 1e-3, all over rows with at
+least one visible key.  Rows with no visible key must be exactly 0 in O and
+-inf in LSE.
+"""
+
+import math
+import sys
+
+import pytest
+import torch
+
+import exact_attention_67_amd as fa
+from oracle import prefix as pre
+from tests import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+TOL = dict(max_abs=2e-2, rel_rms=1e-2, lse=1e-3)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    fa.load()
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _scale(D):
+    return float(torch.tensor(1 / math.sqrt(D), dtype=torch.float32))
+
+
+def _qkv(B, H, Sq, Sk, D, seed):
+    q = wl.make_qkv(B, H, Sq, D, torch.bfloat16, seed=seed)[0]
+    _, k, v = wl.make_qkv(B, H, Sk, D, torch.bfloat16, seed=seed + 1)
+    return q, k, v
+
+
+def check(o, lse, o_ref, lse_ref, label):
+    o64, l64 = o.cpu().double(), lse.cpu().double()
+    empty = torch.isneginf(lse_ref)
+    assert torch.equal(torch.isneginf(l64), empty), f"{label}: empty-row pattern differs"
+    assert torch.all(o64[empty] == 0.0), f"{label}: empty rows not zero"
+    full = ~empty
+    assert torch.isfinite(o64).all() and torch.isfinite(l64[full]).all(), label
+    if not full.any():
+        return
+    err = o64 - o_ref
+    max_abs = err[full].abs().max().item()
+    num = err.pow(2).sum(dim=(-2, -1)).sqrt()
+    den = o_ref.pow(2).sum(dim=(-2, -1)).sqrt().clamp_min(1e-300)
+    has = full.any(dim=-1)
+    rel = (num / den)[has].max().item()
+    lse_err = (l64[full] - lse_ref[full]).abs().max().item()
+    say(f"{label}: max_abs={max_abs:.3e} rel_rms={rel:.3e} lse={lse_err:.3e} "
+        f"empty_rows={int(empty.sum())}")
+    assert max_abs <= TOL["max_abs"], (label, max_abs)
+    assert rel <= TOL["rel_rms"], (label, rel)
+    assert lse_err <= TOL["lse"], (label, lse_err)
+
+
+# ---------------------------------------------------------------------------
+# fa_fwd_kv against the oracle
+# ---------------------------------------------------------------------------
+
+KV_SHAPES = [  # B, H, Sq, Sk
+    (1, 2, 1, 300),      # decode: one query against a prefix
+    (2, 3, 77, 300),     # a chunk shorter than the keys
+    (1, 2, 300, 77),     # more queries than keys: the first 223 rows see nothing
+    (1, 2, 65, 1000),
+    (2, 2, 130, 129),
+]
+KV_CASES = [(B, H, Sq, Sk, D, c) for (B, H, Sq, Sk) in KV_SHAPES for D in (64, 128, 256)
+            for c in (False, True)]
+
+
+@pytest.mark.parametrize("B,H,Sq,Sk,D,causal", KV_CASES,
+                         ids=[f"B{B}H{H}-q{Sq}-k{Sk}-D{D}-{'c' if c else 'n'}"
+                              for B, H, Sq, Sk, D, c in KV_CASES])
+def test_fwd_kv_parity(B, H, Sq, Sk, D, causal):
+    q, k, v = _qkv(B, H, Sq, Sk, D, seed=5000 + Sq + Sk + D)
+    s = _scale(D)
+    o, lse = fa.forward_kv(q.cuda(), k.cuda(), v.cuda(), causal=causal, scale=s)
+    torch.cuda.synchronize()
+    o_ref, l_ref = pre.attention_prefix(q, k, v, causal, s)
+    check(o, lse, o_ref, l_ref, f"kv B={B} H={H} Sq={Sq} Sk={Sk} D={D} causal={causal}")
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_fwd_kv_square_is_fa_fwd_bitwise(D):
+    q, k, v = (t.cuda() for t in wl.make_qkv(2, 2, 333, D, torch.bfloat16, seed=77))
+    for causal in (False, True):
+        o1, l1 = fa.forward(q, k, v, causal=causal)
+        o2, l2 = fa.forward_kv(q, k, v, causal=causal)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("Sq,Sk", [(300, 700), (300, 100)])
+def test_fwd_kv_256_row_workgroups(Sq, Sk):
+    B, H, D = 32, 16, 128
+    assert fa.fa_fwd_plan(B, H, Sq, D, 1, 2)["rows_per_group"] == 256
+    q, k, v = _qkv(B, H, Sq, Sk, D, seed=6000 + Sk)
+    s = _scale(D)
+    o, lse = fa.forward_kv(q.cuda(), k.cuda(), v.cuda(), causal=True, scale=s)
+    torch.cuda.synchronize()
+    o_ref, l_ref = pre.attention_prefix(q, k, v, True, s)
+    check(o, lse, o_ref, l_ref, f"kv 256-row groups Sq={Sq} Sk={Sk}")
+
+
+# ---------------------------------------------------------------------------
+# Compositions through fa_merge
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_chunked_prefill_from_prefix_and_chunk(D):
+    # a chunk of 256 queries after a cached prefix of 1000 keys: the prefix is
+    # fully visible (no mask), the chunk causal; merged = causal attention of
+    # the chunk against all 1256 keys
+    B, H, P, C = 1, 4, 1000, 256
+    q, k, v = _qkv(B, H, C, P + C, D, seed=7000 + D)
+    s = _scale(D)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    o_parts = torch.empty((2, B, H, C, D), dtype=torch.bfloat16, device="cuda")
+    l_parts = torch.empty((2, B, H, C), dtype=torch.float32, device="cuda")
+    fa.forward_kv(qd, kd[:, :, :P].contiguous(), vd[:, :, :P].contiguous(), causal=False,
+                  scale=s, out=o_parts[0], lse=l_parts[0])
+    fa.forward_kv(qd, kd[:, :, P:].contiguous(), vd[:, :, P:].contiguous(), causal=True,
+                  scale=s, out=o_parts[1], lse=l_parts[1])
+    o, lse = fa.merge(o_parts, l_parts)
+    direct_o, direct_l = fa.forward_kv(qd, kd, vd, causal=True, scale=s)
+    torch.cuda.synchronize()
+    o_ref, l_ref = pre.attention_prefix(q, k, v, True, s)
+    check(o, lse, o_ref, l_ref, f"prefill via merge D={D}")
+    check(direct_o, direct_l, o_ref, l_ref, f"prefill direct D={D}")
+
+
+def test_decode_split_over_key_shards():
+    B, H, D, Sk, G = 4, 8, 128, 4000, 5
+    q, k, v = _qkv(B, H, 1, Sk, D, seed=8000)
+    s = _scale(D)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    cuts = [0, 700, 1500, 1501, 3100, Sk]          # uneven shards, one of one key
+    o_parts = torch.empty((G, B, H, 1, D), dtype=torch.bfloat16, device="cuda")
+    l_parts = torch.empty((G, B, H, 1), dtype=torch.float32, device="cuda")
+    for g in range(G):
+        a, b = cuts[g], cuts[g + 1]
+        fa.forward_kv(qd, kd[:, :, a:b].contiguous(), vd[:, :, a:b].contiguous(), causal=True,
+                      scale=s, out=o_parts[g], lse=l_parts[g])
+    o, lse = fa.merge(o_parts, l_parts)
+    torch.cuda.synchronize()
+    o_ref, l_ref = pre.attention_prefix(q, k, v, True, s)
+    check(o, lse, o_ref, l_ref, "decode split over 5 key shards")
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_merge_synthetic_parts(D):
+    G, B, H, S = 4, 2, 3, 257
+    g = torch.Generator().manual_seed(9000 + D)
+    o_parts = torch.randn((G, B, H, S, D), generator=g).to(torch.bfloat16)
+    l_parts = (torch.randn((G, B, H, S), generator=g) * 6.0).float()
+    l_parts[1, 0, 0, :50] = -math.inf           # empty parts for some rows
+    l_parts[:, 1, 2, 7] = -math.inf             # a row empty in every part
+    o_ref, l_ref = pre.merge_reference(o_parts, l_parts)
+    # the kernel must not read a part whose weight is 0: poison those O rows
+    o_poison = o_parts.clone()
+    o_poison[1, 0, 0, :50] = float("nan")
+    o_poison[:, 1, 2, 7] = float("nan")
+    o, lse = fa.merge(o_poison.cuda(), l_parts.cuda())
+    torch.cuda.synchronize()
+    check(o, lse, o_ref, l_ref, f"merge synthetic D={D}")
+    full = torch.isfinite(l_ref)
+    assert (lse.cpu().double()[full] - l_ref[full]).abs().max().item() <= 1e-5
+
+
+def test_merge_single_part_is_identity_up_to_rounding():
+    o_parts = wl.make_qkv(2, 2, 100, 128, torch.bfloat16, seed=3)[0].view(1, 2, 2, 100, 128)
+    l_parts = torch.randn((1, 2, 2, 100), generator=torch.Generator().manual_seed(4)).float()
+    o, lse = fa.merge(o_parts.cuda(), l_parts.cuda())
+    torch.cuda.synchronize()
+    assert torch.equal(o.cpu(), o_parts[0])
+    assert torch.allclose(lse.cpu(), l_parts[0], rtol=0, atol=1e-6)
+
+
+def test_bad_arguments_rejected_before_launch():
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros(1, 1, 16, 64, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(fa.FAError):
+        fa.forward_kv(q, k, k, causal=True, scale=-1.0)
+    with pytest.raises(ValueError):
+        fa.forward_kv(q, k[:, :, :, :32].contiguous(), k[:, :, :, :32].contiguous())
+    op = torch.zeros(2, 1, 1, 8, 64, dtype=torch.bfloat16, device="cuda")
+    lp = torch.zeros(2, 1, 1, 8, dtype=torch.float32, device="cuda")
+    with pytest.raises(fa.FAError):
+        fa.merge(op, lp, out=op[0])              # output aliases the parts

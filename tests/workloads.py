@@ -98,3 +98,83 @@ def make_qkv(B: int, H: int, S: int, D: int, dtype: torch.dtype, seed: int,
     if device != "cpu":
         q, k, v = (t.to(device) for t in (q, k, v))
     return q, k, v
+
+
+# ---------------------------------------------------------------------------
+# Queries against a key prefix and merges over key sets (measurement shapes)
+# ---------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class PrefixWorkload:
+    """Sq bf16 queries against Sk keys per (batch, head); the queries are the
+    last Sq positions of the Sk-position sequence (chunked prefill, decode)."""
+    name: str
+    B: int
+    H: int
+    Sq: int
+    Sk: int
+    D: int
+    causal: bool
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return float(torch.tensor(1.0 / math.sqrt(self.D), dtype=torch.float32))
+
+    def visible_pairs(self) -> int:
+        """(query, key) pairs the mask keeps, per (batch, head)."""
+        if not self.causal:
+            return self.Sq * self.Sk
+        shift = self.Sk - self.Sq
+        return sum(max(0, min(self.Sk, i + shift + 1)) for i in range(self.Sq))
+
+    def flops(self) -> float:
+        """Nominal flops: 4*D per visible (query, key) pair."""
+        return 4.0 * self.D * self.visible_pairs() * self.B * self.H
+
+    def kv_bytes(self) -> int:
+        return 2 * self.B * self.H * self.Sk * self.D * 2
+
+
+PREFIX_WORKLOADS: Dict[str, PrefixWorkload] = {
+    "prefill_bf16_causal_1x32_q2048_k16384_d128": PrefixWorkload(
+        "prefill_bf16_causal_1x32_q2048_k16384_d128", 1, 32, 2048, 16384, 128, True, 11),
+    "decode_bf16_causal_16x32_q1_k8192_d128": PrefixWorkload(
+        "decode_bf16_causal_16x32_q1_k8192_d128", 16, 32, 1, 8192, 128, True, 12),
+}
+
+
+def make_prefix_inputs(w: PrefixWorkload, device: str = "cpu"):
+    """q [B,H,Sq,D] from seed w.seed; k, v [B,H,Sk,D] from seed w.seed + 1000."""
+    q = make_qkv(w.B, w.H, w.Sq, w.D, torch.bfloat16, w.seed, device=device)[0]
+    _, k, v = make_qkv(w.B, w.H, w.Sk, w.D, torch.bfloat16, w.seed + 1000, device=device)
+    return q, k, v
+
+
+@dataclass(frozen=True)
+class MergeWorkload:
+    """G partial results (bf16 O, float32 LSE) of [B,H,S,D] to merge."""
+    name: str
+    G: int
+    B: int
+    H: int
+    S: int
+    D: int
+    seed: int
+
+    def bytes_moved(self) -> int:
+        rows = self.B * self.H * self.S
+        return self.G * rows * (self.D * 2 + 4) + rows * (self.D * 2 + 4)
+
+
+MERGE_WORKLOADS: Dict[str, MergeWorkload] = {
+    "merge_g4_1x32x16384x128": MergeWorkload("merge_g4_1x32x16384x128", 4, 1, 32, 16384, 128, 13),
+}
+
+
+def make_merge_inputs(w: MergeWorkload, device: str = "cpu"):
+    """o_parts bf16 N(0,1) [G,B,H,S,D]; lse_parts float32 N(0,1)*4 [G,B,H,S]."""
+    g = torch.Generator("cpu").manual_seed(w.seed)
+    o = torch.randn((w.G, w.B, w.H, w.S, w.D), generator=g, dtype=torch.float32)
+    l = torch.randn((w.G, w.B, w.H, w.S), generator=g, dtype=torch.float32) * 4.0
+    return o.to(torch.bfloat16).to(device), l.to(device)
