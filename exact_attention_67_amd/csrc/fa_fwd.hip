@@ -1112,10 +1112,11 @@ int fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, i
 // ----------------------------------------------------------------------------
 // LSE = log sum_g exp(LSE_g), O = sum_g exp(LSE_g - LSE) O_g, per output row.
 // One thread per 16 bytes (8 bf16) of an output row: 16-byte loads of each
-// part's O, float32 weights and sums, one bf16 (round to nearest even) store.
+// part's O (for up to 16 parts all issued before any is used), float32
+// weights and sums, one bf16 (round to nearest even) store.
 // A part whose weight is 0 (LSE_g = -inf, or underflow) is skipped and its O
 // is not read.  A row with no visible key in any part: O = 0, LSE = -inf.
-template <int D>
+template <int D, int GU>  // GU > 0: G <= GU parts, unrolled; GU = 0: any G
 __global__ __launch_bounds__(256) void fa_merge_kernel(const uint16_t* __restrict__ Op,
                                                        const float* __restrict__ Lp, int G,
                                                        int64_t rows, uint16_t* __restrict__ O,
@@ -1125,22 +1126,55 @@ __global__ __launch_bounds__(256) void fa_merge_kernel(const uint16_t* __restric
   if (t >= rows * CPR) return;
   const int64_t r = t / CPR;
   const int ch = (int)(t % CPR);
-  float m = -INFINITY;
-  for (int g = 0; g < G; ++g) m = fmaxf(m, Lp[g * rows + r]);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float lse = -INFINITY;
-  if (m != -INFINITY) {
-    float sum = 0.0f;
-    for (int g = 0; g < G; ++g) sum += fast_exp2((Lp[g * rows + r] - m) * kLog2e);
-    lse = m + fast_log2(sum) * kLn2;
-    for (int g = 0; g < G; ++g) {
-      const float w = fast_exp2((Lp[g * rows + r] - lse) * kLog2e);
-      if (w == 0.0f) continue;
-      const u32x4 raw = *reinterpret_cast<const u32x4*>(Op + (g * rows + r) * D + ch * 8);
+  auto add = [&](const u32x4 raw, const float w) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[2 * e] += w * __builtin_bit_cast(float, raw[e] << 16);
-        acc[2 * e + 1] += w * __builtin_bit_cast(float, raw[e] & 0xFFFF0000u);
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] += w * __builtin_bit_cast(float, raw[e] << 16);
+      acc[2 * e + 1] += w * __builtin_bit_cast(float, raw[e] & 0xFFFF0000u);
+    }
+  };
+  if constexpr (GU > 0) {
+    // All parts' LSEs, then all parts' 16-byte loads in flight together.
+    float lg[GU];
+    float m = -INFINITY;
+#pragma unroll
+    for (int g = 0; g < GU; ++g) {
+      const float x = Lp[(g < G ? g : G - 1) * rows + r];  // index kept in range
+      lg[g] = g < G ? x : -INFINITY;
+      m = fmaxf(m, lg[g]);
+    }
+    if (m != -INFINITY) {
+      float sum = 0.0f;
+#pragma unroll
+      for (int g = 0; g < GU; ++g) sum += fast_exp2((lg[g] - m) * kLog2e);
+      lse = m + fast_log2(sum) * kLn2;
+      float w[GU];
+      u32x4 raw[GU];
+#pragma unroll
+      for (int g = 0; g < GU; ++g) {
+        w[g] = fast_exp2((lg[g] - lse) * kLog2e);
+        raw[g] = u32x4{0u, 0u, 0u, 0u};
+        if (w[g] != 0.0f)
+          raw[g] = *reinterpret_cast<const u32x4*>(Op + ((g < G ? g : G - 1) * rows + r) * D +
+                                                    ch * 8);
+      }
+#pragma unroll
+      for (int g = 0; g < GU; ++g)
+        if (w[g] != 0.0f) add(raw[g], w[g]);
+    }
+  } else {
+    float m = -INFINITY;
+    for (int g = 0; g < G; ++g) m = fmaxf(m, Lp[g * rows + r]);
+    if (m != -INFINITY) {
+      float sum = 0.0f;
+      for (int g = 0; g < G; ++g) sum += fast_exp2((Lp[g * rows + r] - m) * kLog2e);
+      lse = m + fast_log2(sum) * kLn2;
+      for (int g = 0; g < G; ++g) {
+        const float w = fast_exp2((Lp[g * rows + r] - lse) * kLog2e);
+        if (w == 0.0f) continue;
+        add(*reinterpret_cast<const u32x4*>(Op + (g * rows + r) * D + ch * 8), w);
       }
     }
   }
@@ -1151,6 +1185,16 @@ __global__ __launch_bounds__(256) void fa_merge_kernel(const uint16_t* __restric
              ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[2 * e + 1]) << 16);
   *reinterpret_cast<u32x4*>(O + r * D + ch * 8) = out;
   if (ch == 0) L[r] = lse;
+}
+
+template <int D>
+int run_merge(const uint16_t* Op, const float* Lp, int G, int64_t rows, uint16_t* O, float* L,
+              hipStream_t s) {
+  const unsigned grid = (unsigned)((rows * (D / 8) + 255) / 256);
+  if (G <= 4) return launch(fa_merge_kernel<D, 4>, grid, 256, s, Op, Lp, G, rows, O, L);
+  if (G <= 8) return launch(fa_merge_kernel<D, 8>, grid, 256, s, Op, Lp, G, rows, O, L);
+  if (G <= 16) return launch(fa_merge_kernel<D, 16>, grid, 256, s, Op, Lp, G, rows, O, L);
+  return launch(fa_merge_kernel<D, 0>, grid, 256, s, Op, Lp, G, rows, O, L);
 }
 
 }  // namespace
@@ -1182,14 +1226,13 @@ extern "C" int fa_merge(const void* o_parts, const float* lse_parts, int G, int 
       ranges_overlap(lse, lb, o_parts, ob * G) || ranges_overlap(lse, lb, lse_parts, lb * G) ||
       ranges_overlap(o, ob, lse, lb))
     return FA_ERR_ALIAS;
-  const unsigned grid = (unsigned)((rows * (D / 8) + 255) / 256);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const uint16_t* Op = static_cast<const uint16_t*>(o_parts);
   uint16_t* Out = static_cast<uint16_t*>(o);
   switch (D) {
-    case 64: return launch(fa_merge_kernel<64>, grid, 256, s, Op, lse_parts, G, rows, Out, lse);
-    case 128: return launch(fa_merge_kernel<128>, grid, 256, s, Op, lse_parts, G, rows, Out, lse);
-    default: return launch(fa_merge_kernel<256>, grid, 256, s, Op, lse_parts, G, rows, Out, lse);
+    case 64: return run_merge<64>(Op, lse_parts, G, rows, Out, lse, s);
+    case 128: return run_merge<128>(Op, lse_parts, G, rows, Out, lse, s);
+    default: return run_merge<256>(Op, lse_parts, G, rows, Out, lse, s);
   }
 }
 

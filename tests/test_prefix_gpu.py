@@ -161,10 +161,13 @@ def test_decode_split_over_key_shards():
     check(o, lse, o_ref, l_ref, "decode split over 5 key shards")
 
 
-@pytest.mark.parametrize("D", [64, 128, 256])
-def test_merge_synthetic_parts(D):
-    G, B, H, S = 4, 2, 3, 257
-    g = torch.Generator().manual_seed(9000 + D)
+MERGE_CASES = [(4, 64), (4, 128), (4, 256), (7, 128), (12, 128), (20, 64)]  # parts, D
+
+
+@pytest.mark.parametrize("G,D", MERGE_CASES, ids=[f"G{g}-D{d}" for g, d in MERGE_CASES])
+def test_merge_synthetic_parts(G, D):
+    B, H, S = 2, 3, 257
+    g = torch.Generator().manual_seed(9000 + D + G)
     o_parts = torch.randn((G, B, H, S, D), generator=g).to(torch.bfloat16)
     l_parts = (torch.randn((G, B, H, S), generator=g) * 6.0).float()
     l_parts[1, 0, 0, :50] = -math.inf           # empty parts for some rows
@@ -176,7 +179,7 @@ def test_merge_synthetic_parts(D):
     o_poison[:, 1, 2, 7] = float("nan")
     o, lse = fa.merge(o_poison.cuda(), l_parts.cuda())
     torch.cuda.synchronize()
-    check(o, lse, o_ref, l_ref, f"merge synthetic D={D}")
+    check(o, lse, o_ref, l_ref, f"merge synthetic G={G} D={D}")
     full = torch.isfinite(l_ref)
     assert (lse.cpu().double()[full] - l_ref[full]).abs().max().item() <= 1e-5
 
