@@ -254,6 +254,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the Sq != Sk and merge workloads")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache launches (profiling runs count warm launches only)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     a = ap.parse_args()
@@ -279,17 +281,25 @@ def main():
     w = wl.WORKLOADS[a.workload]
     causal = (not a.noncausal) and (True in w.causal)
     log(f"[bench] {w.name} causal={causal} steps={a.steps} warmup={a.warmup}")
-    r = time_workload(w, causal, a.steps, a.warmup, cold_launches=min(20, a.steps))
+    r = time_workload(w, causal, a.steps, a.warmup,
+                      cold_launches=0 if a.no_cold else min(20, a.steps))
     flops = w.flops(causal)
     value = flops / (r["ms_per_step"] * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == torch.bfloat16 else PEAK_F32_TFLOPS
     achieved = flops / (r["launch_ms_avg"] * 1e-3) / 1e12
     log(f"[bench] ms/step={r['ms_per_step']:.4f} launch avg={r['launch_ms_avg']:.4f} "
         f"min={r['launch_ms_min']:.4f} med={r['launch_ms_med']:.4f} -> {value:.1f} TFLOP/s "
-        f"({100 * value / peak:.1f}% of peak); cold med={r['cold_ms_med']:.4f}")
-    cold_diff = 100.0 * (r["cold_ms_med"] - r["launch_ms_med"]) / r["launch_ms_med"]
-    if abs(cold_diff) > 5.0:
-        log(f"[bench] warm and cold launches differ by {cold_diff:.1f}%")
+        f"({100 * value / peak:.1f}% of peak)")
+    cold = None
+    if "cold_ms_med" in r:
+        cold_diff = 100.0 * (r["cold_ms_med"] - r["launch_ms_med"]) / r["launch_ms_med"]
+        log(f"[bench] cold launch median {r['cold_ms_med']:.4f} ms ({cold_diff:+.1f}% vs warm)")
+        if abs(cold_diff) > 5.0:
+            log(f"[bench] warm and cold launches differ by {cold_diff:.1f}%")
+        cold = {"evict_bytes": COLD_EVICT_BYTES,
+                "launch_ms_median": round(r["cold_ms_med"], 5),
+                "launch_ms_min": round(r["cold_ms_min"], 5),
+                "cold_vs_warm_pct": round(cold_diff, 2)}
     sclk = recorded_profile_value(w.name, "sclk_mhz_under_load")
 
     if a.all:
@@ -345,12 +355,7 @@ def main():
             "peak_at_sclk": round(peak * sclk / NOMINAL_SCLK_MHZ, 1) if sclk else None,
             "frac_at_sclk": round(achieved / (peak * sclk / NOMINAL_SCLK_MHZ), 4) if sclk else None,
         },
-        "cold": {
-            "evict_bytes": COLD_EVICT_BYTES,
-            "launch_ms_median": round(r["cold_ms_med"], 5),
-            "launch_ms_min": round(r["cold_ms_min"], 5),
-            "cold_vs_warm_pct": round(cold_diff, 2),
-        },
+        "cold": cold,
         "cpu_baseline": cpu,
         # not part of `value`: the Sq != Sk path and the merge on their own workloads
         "secondary": secondary,
