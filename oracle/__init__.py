@@ -14,3 +14,4 @@ from .prefix import (  # noqa: F401
     merge_reference,
     prefix_keep_mask,
 )
+from .backward import attention_backward, attention_delta  # noqa: F401
