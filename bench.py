@@ -31,7 +31,8 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X published dense bf16 matrix peak
 PEAK_F32_TFLOPS = 157.3     # MI355X published fp32 matrix peak
 PEAK_HBM_GBS = 8000.0       # MI355X published HBM3E bandwidth
 DEFAULT_WORKLOAD = "c4_bf16_causal_1x32x16384x128"
-SRC = os.path.join(ROOT, "exact_attention_67_amd", "csrc", "fa_fwd.hip")
+# sources of the forward kernels (the profile summaries are keyed to them)
+SRCS = [os.path.join(ROOT, "exact_attention_67_amd", "csrc", n) for n in ("fa_fwd.hip", "fa_device.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_bf16_c4_hbm_traffic.txt")
 NOMINAL_SCLK_MHZ = 2400.0   # clock of the published peak
 COLD_EVICT_BYTES = 512 << 20
@@ -42,8 +43,11 @@ def log(*a):
 
 
 def source_digest() -> str:
-    with open(SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for p in SRCS:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def recorded_profile_value(workload: str, key: str):

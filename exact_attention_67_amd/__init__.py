@@ -29,6 +29,7 @@ from ._lib import (  # noqa: F401
     LIB_PATH,
     FAError,
     fa_fwd,
+    fa_bwd,
     fa_fwd_f32,
     fa_fwd_kv,
     fa_fwd_plan,
@@ -37,8 +38,8 @@ from ._lib import (  # noqa: F401
     status_str,
 )
 
-__all__ = ["forward", "forward_kv", "merge", "fa_fwd", "fa_fwd_f32", "fa_fwd_kv", "fa_merge",
-           "fa_fwd_plan", "load", "status_str", "FAError"]
+__all__ = ["forward", "forward_kv", "merge", "backward", "fa_fwd", "fa_fwd_f32", "fa_fwd_kv",
+           "fa_merge", "fa_bwd", "fa_fwd_plan", "load", "status_str", "FAError"]
 
 
 def forward(q, k, v, causal: bool = True, scale: Optional[float] = None,
@@ -152,3 +153,37 @@ def merge(o_parts, lse_parts, out=None, lse=None, stream=None) -> Tuple[object, 
     if st != FA_OK:
         raise FAError(st, "fa_merge")
     return out, lse
+
+
+def backward(q, k, v, o, lse, dout, causal: bool = True, scale: Optional[float] = None,
+             stream=None) -> Tuple[object, object, object]:
+    """Gradients (dq, dk, dv) of the bf16 forward for incoming gradient dout.
+
+    q, k, v, o, dout: bf16 [B, H, S, D]; lse: float32 [B, H, S] (the forward's
+    outputs o and lse, same causal and scale).  The Delta buffer the kernels
+    need is allocated here with torch and discarded."""
+    import torch
+
+    ts = (q, k, v, o, dout)
+    if not all(t.is_cuda for t in ts + (lse,)):
+        raise ValueError("inputs must be GPU tensors")
+    if not all(t.dtype == torch.bfloat16 for t in ts) or lse.dtype != torch.float32:
+        raise ValueError("q, k, v, o, dout must be bf16 and lse float32")
+    if q.dim() != 4 or any(t.shape != q.shape for t in ts):
+        raise ValueError("q, k, v, o, dout must all be [B, H, S, D] of one shape")
+    B, H, S, D = (int(x) for x in q.shape)
+    if tuple(lse.shape) != (B, H, S):
+        raise ValueError("lse must be [B, H, S]")
+    if not all(t.is_contiguous() for t in ts + (lse,)):
+        raise ValueError("inputs must be contiguous")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    s = _stream(stream, q.device)
+    st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+                B, H, S, D, int(bool(causal)), float(scale), s.cuda_stream)
+    if st != FA_OK:
+        raise FAError(st, "fa_bwd")
+    return dq, dk, dv

@@ -26,8 +26,8 @@ FA_ERR_ALIGN = 6
 FA_ERR_ALIAS = 7
 FA_ERR_LAUNCH = 8
 
-EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_kv", "fa_merge", "fa_fwd_plan", "fa_status_str",
-           "fa_abi_version")
+EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_kv", "fa_merge", "fa_bwd", "fa_fwd_plan",
+           "fa_status_str", "fa_abi_version")
 ABI_VERSION = 1
 
 _lock = threading.Lock()
@@ -53,6 +53,8 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.fa_fwd_kv.restype = i
     lib.fa_merge.argtypes = [vp, vp, i, i, i, i, i, vp, vp, vp]
     lib.fa_merge.restype = i
+    lib.fa_bwd.argtypes = [vp] * 10 + [i, i, i, i, i, f, vp]
+    lib.fa_bwd.restype = i
     ip = ctypes.POINTER(i)
     lib.fa_fwd_plan.argtypes = [i, i, i, i, i, i, ip, ip, ip, ip]
     lib.fa_fwd_plan.restype = i
@@ -108,6 +110,14 @@ def fa_merge(o_parts: int, lse_parts: int, G: int, B: int, H: int, S: int, D: in
              lse: int, stream: int | None) -> int:
     """Raw C call on device addresses (ints).  Returns the fa_status."""
     return load().fa_merge(o_parts, lse_parts, G, B, H, S, D, o, lse, stream)
+
+
+def fa_bwd(q: int, k: int, v: int, o: int, dout: int, lse: int, dq: int, dk: int, dv: int,
+           delta: int, B: int, H: int, S: int, D: int, causal: int, scale: float,
+           stream: int | None) -> int:
+    """Raw C call on device addresses (ints).  Returns the fa_status."""
+    return load().fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, S, D, causal, scale,
+                         stream)
 
 
 def fa_fwd_plan(B: int, H: int, S: int, D: int, causal: int, elem_bytes: int) -> dict:

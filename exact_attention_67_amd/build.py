@@ -1,6 +1,7 @@
 """Build the HIP library in-tree: exact_attention_67_amd/libfa_mi355x.so.
 
-Compiles csrc/fa_fwd.hip for gfx950 only with hipcc.  Packed-fp32 code
+Compiles the HIP sources in csrc/ (forward and backward kernels, host entry
+points) into one shared library, for gfx950 only, with hipcc.  Packed-fp32 code
 generation is switched off for device code (the host pass warns that it does
 not know the feature; that warning is harmless).
 
@@ -17,7 +18,8 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "fa_fwd.hip")
+CSRC = os.path.join(PKG, "csrc")
+SOURCES = [os.path.join(CSRC, "fa_fwd.hip"), os.path.join(CSRC, "fa_bwd.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libfa_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
@@ -40,13 +42,15 @@ def compile_flags() -> list:
         "-Wall",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-I", INCLUDE,
+        "-I", CSRC,
     ]
 
 
 def build(verbose: bool = False, save_temps: str | None = None) -> str:
     """Compile the library; always recompiles.  Returns the .so path."""
     tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), *compile_flags(), "-shared", SRC, "-o", tmp]
+    cmd = [hipcc(), *compile_flags(), "-shared", *[src for src in SOURCES if os.path.exists(src)],
+           "-o", tmp]
     if save_temps:
         os.makedirs(save_temps, exist_ok=True)
         cmd.insert(1, "-save-temps=cwd")

@@ -1,0 +1,506 @@
+// Attention backward for MI355X (gfx950): dq, dk, dv of the fused forward.
+//
+// The pages ("Profiling in PyTorch (Part 3): Attention is all you profile",
+// the "FlashAttention-2" blog) only say that the fused kernels serve training
+// too; the computation here is the gradient of the forward definition
+// (matmul, scale, causal mask, softmax, matmul), the same steps the
+// FlashAttention-2 blog's fused forward avoids materialising:
+//
+//   P     = exp(scale * q k^T - LSE)      (recomputed from q, k and the saved LSE)
+//   dv    = P^T dO
+//   dP    = dO v^T
+//   Delta = rowsum(dO * O)
+//   dS    = P * (dP - Delta)
+//   dq    = scale * dS k,   dk = scale * dS^T q
+//
+// Three kernels:
+//  * fa_bwd_delta_kernel: Delta (one row per TPR consecutive lanes).
+//  * fa_bwd_dkdv_kernel: one workgroup of 4 wavefronts per (block of 128 keys,
+//    head, batch); each wave owns 32 keys and keeps their K and V fragments and
+//    dK, dV accumulators in registers, while tiles of queries (q and dO, plus
+//    their LSE and Delta) stream through LDS.  S = q K^T and dP = dO V^T come
+//    out with one key per lane (the forward's S^T = K Q^T with the roles of
+//    queries and keys exchanged), so P and dS are per-lane columns; dV += P^T dO
+//    and dK += dS^T q read dO and q with the transposing LDS read.  q and dO
+//    are each needed both row-wise and transposed, so each query tile is
+//    copied into LDS twice, once per swizzle.
+//  * fa_bwd_dq_kernel: the forward's layout (one query per lane): S^T = K q^T,
+//    dP^T = V dO^T, dS^T, then dq^T += K^T dS^T with K read transposed.
+// No atomics and no workspace beyond the caller's Delta buffer: dq is
+// accumulated by the workgroup that owns the query tile.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "fa.h"
+#include "fa_device.h"
+
+namespace {
+
+// ----------------------------------------------------------------------------
+// Delta = rowsum(dO * O)
+// ----------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void fa_bwd_delta_kernel(const uint16_t* __restrict__ O,
+                                                           const uint16_t* __restrict__ dO,
+                                                           float* __restrict__ Delta,
+                                                           int64_t rows) {
+  constexpr int TPR = D / 8;  // lanes per row, 8 elements (16 bytes) each
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t r = t / TPR;
+  const int c = (int)(t % TPR);
+  float acc = 0.0f;
+  if (r < rows) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(O + r * D + c * 8);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(dO + r * D + c * 8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc = fmaf(__builtin_bit_cast(float, a[e] << 16), __builtin_bit_cast(float, b[e] << 16), acc);
+      acc = fmaf(__builtin_bit_cast(float, a[e] & 0xFFFF0000u),
+                 __builtin_bit_cast(float, b[e] & 0xFFFF0000u), acc);
+    }
+  }
+  // sum over the TPR consecutive lanes of the row (all lanes take part)
+#pragma unroll
+  for (int m = TPR / 2; m > 0; m >>= 1) acc += __shfl_xor(acc, m);
+  if (r < rows && c == 0) Delta[r] = acc;
+}
+
+// Copy of 64 floats (one per query row of a tile) into LDS: lane l copies
+// src[min(row0 + l, S - 1)].
+__device__ __forceinline__ void issue_rowvec(const float* __restrict__ src, lds_u8* dst, int row0,
+                                             int S, int lane) {
+  const void* gp = src + min(row0 + lane, S - 1);
+  __builtin_amdgcn_global_load_lds(gp, dst, 4, 0, 0);
+}
+
+typedef __attribute__((address_space(3))) float lds_f32;
+
+// bf16 O^T-layout accumulator column (lane = row `row` of the output, 16
+// registers per 32-wide block) scaled and stored to out[row][0..D).
+template <int DB>
+__device__ __forceinline__ void store_col(uint16_t* __restrict__ out_row, const f32x16 (&acc)[DB],
+                                          float mul, int hh) {
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      u32x2 pk;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const __bf16 lo = (__bf16)(acc[db][gq * 4 + 2 * t] * mul);
+        const __bf16 hi = (__bf16)(acc[db][gq * 4 + 2 * t + 1] * mul);
+        pk[t] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+                ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+      }
+      *reinterpret_cast<u32x2*>(out_row + db * 32 + gq * 8 + hh * 4) = pk;
+    }
+}
+
+// acc[db] += A^T * Bfrag, A read transposed from a V-swizzled tile (rows =
+// the contraction index, 16 per step), the forward's P*V pattern.
+template <class C>
+__device__ __forceinline__ void tr_product(f32x16 (&acc)[C::DB], const lds_u8* tile,
+                                           const bf16x8 (&bf)[C::PCH],
+                                           const int (&v_off)[C::NVOFF]) {
+#pragma unroll
+  for (int pc = 0; pc < C::PCH; ++pc)
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      const lds_u8* p = tile + pc * 16 * C::ROW_BYTES + (db / C::NVOFF) * 256 +
+                        v_off[db % C::NVOFF];
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * C::ROW_BYTES));
+      const bf16x8 af =
+          __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf[pc], acc[db], 0, 0, 0);
+    }
+}
+
+// Per-lane byte offsets for the row reads (A operand of qk_tile, rows read in
+// the permuted order) and the transposing reads of a tile; as in the forward.
+template <class C>
+__device__ __forceinline__ void operand_offsets(int lane, int (&k_off)[C::NKOFF],
+                                                int (&v_off)[C::NVOFF]) {
+  const int m = lane & 31, hh = lane >> 5;
+  const int pm = key_perm(m);
+  const int ksw = kswz<C>(pm);
+#pragma unroll
+  for (int b = 0; b < C::NKOFF; ++b) k_off[b] = pm * C::ROW_BYTES + (((2 * b + hh) ^ ksw) << 4);
+  const int g = lane >> 4, j4 = (lane >> 2) & 3, t4 = lane & 3;
+  const int vx = 2 * (g & 1) + (t4 >> 1);
+  const int vsw = vswz<C>(hh * 8 + j4);
+  const int v_row = (hh * 8 + j4) * C::ROW_BYTES + (t4 & 1) * 8;
+#pragma unroll
+  for (int d4 = 0; d4 < C::NVOFF; ++d4) v_off[d4] = v_row + (((4 * d4 + vx) ^ vsw) << 4);
+}
+
+// Fragments of one row (lane's row `row` of a [S, D] matrix) as the B operand
+// of qk_tile: lane holds X[row][ch*16 + hh*8 .. +8]; zero past the end.
+template <class C>
+__device__ __forceinline__ void row_fragments(bf16x8 (&f)[C::KCH], const uint16_t* __restrict__ X,
+                                              int row, int S, int hh) {
+#pragma unroll
+  for (int ch = 0; ch < C::KCH; ++ch) {
+    u32x4 raw = u32x4{0u, 0u, 0u, 0u};
+    if (row < S) raw = *reinterpret_cast<const u32x4*>(X + (size_t)row * C::D + ch * 16 + hh * 8);
+    f[ch] = __builtin_bit_cast(bf16x8, raw);
+  }
+}
+
+// ----------------------------------------------------------------------------
+// dK, dV: one workgroup per (128 keys, head, batch)
+// ----------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void fa_bwd_dkdv_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+    const float* __restrict__ LSE, const float* __restrict__ Delta, uint16_t* __restrict__ dK,
+    uint16_t* __restrict__ dV, int S, int nk, int bh_total, int group_heads, float c,
+    float scale) {
+  using C = BfCfg<D, 64, 4>;  // query tiles of 64 rows; 4 waves of 32 keys
+  // Query tile in two layouts (row reads: K swizzle; transposed reads: V
+  // swizzle) for q and dO, two stages; each a separately named array.
+  __shared__ __attribute__((aligned(1024))) uint8_t qr0_raw[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t qr1_raw[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t qt0_raw[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t qt1_raw[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t dr0_raw[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t dr1_raw[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t dt0_raw[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t dt1_raw[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(256))) uint8_t ls0_raw[256];
+  __shared__ __attribute__((aligned(256))) uint8_t ls1_raw[256];
+  __shared__ __attribute__((aligned(256))) uint8_t de0_raw[256];
+  __shared__ __attribute__((aligned(256))) uint8_t de1_raw[256];
+  lds_u8* qr0 = (lds_u8*)qr0_raw;
+  lds_u8* qr1 = (lds_u8*)qr1_raw;
+  lds_u8* qt0 = (lds_u8*)qt0_raw;
+  lds_u8* qt1 = (lds_u8*)qt1_raw;
+  lds_u8* dr0 = (lds_u8*)dr0_raw;
+  lds_u8* dr1 = (lds_u8*)dr1_raw;
+  lds_u8* dt0 = (lds_u8*)dt0_raw;
+  lds_u8* dt1 = (lds_u8*)dt1_raw;
+  lds_u8* ls0 = (lds_u8*)ls0_raw;
+  lds_u8* ls1 = (lds_u8*)ls1_raw;
+  lds_u8* de0 = (lds_u8*)de0_raw;
+  lds_u8* de1 = (lds_u8*)de1_raw;
+
+  // Heaviest key blocks (the first ones, seen by most query tiles) first.
+  int bh, kt;
+  decode_tile<CAUSAL>(xcd_logical_index(blockIdx.x, nk * bh_total), nk, bh_total, group_heads,
+                      bh, kt);
+  if (CAUSAL) kt = nk - 1 - kt;
+
+  const size_t head = (size_t)bh * (size_t)S * D;
+  const uint16_t* Qh = Q + head;
+  const uint16_t* Kh = K + head;
+  const uint16_t* Vh = V + head;
+  const uint16_t* dOh = dO + head;
+  const float* LSEh = LSE + (size_t)bh * S;
+  const float* Dh = Delta + (size_t)bh * S;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int m = lane & 31;
+  const int hh = lane >> 5;
+  const int k0 = kt * 128;
+  const int kw0 = k0 + wave * kRowsPerWave;
+  const int my_k = kw0 + m;
+
+  // Query tiles this workgroup visits: causal -- those with a query >= k0.
+  const int nt = (S + 63) / 64;
+  const int t_first = CAUSAL ? k0 / 64 : 0;
+
+  int qoff[C::LOADS_PER_WAVE], qrow[C::LOADS_PER_WAVE];
+  int toff[C::LOADS_PER_WAVE], trow[C::LOADS_PER_WAVE];
+  tile_offsets<C, false>(qoff, qrow, wave, lane);
+  tile_offsets<C, true>(toff, trow, wave, lane);
+  auto copies = [&](int t, lds_u8* qr, lds_u8* qt, lds_u8* dr, lds_u8* dt, lds_u8* ls,
+                    lds_u8* de) {
+    const int q0 = t * 64;
+    issue_tile<C>(Qh, qr, q0, S, wave, qoff, qrow);
+    issue_tile<C>(Qh, qt, q0, S, wave, toff, trow);
+    issue_tile<C>(dOh, dr, q0, S, wave, qoff, qrow);
+    issue_tile<C>(dOh, dt, q0, S, wave, toff, trow);
+    if (wave == 0) issue_rowvec(LSEh, ls, q0, S, lane);
+    if (wave == 1) issue_rowvec(Dh, de, q0, S, lane);
+  };
+
+  bf16x8 kf[C::KCH], vf[C::KCH];
+  row_fragments<C>(kf, Kh, my_k, S, hh);
+  row_fragments<C>(vf, Vh, my_k, S, hh);
+  int k_off[C::NKOFF], v_off[C::NVOFF];
+  operand_offsets<C>(lane, k_off, v_off);
+
+  f32x16 dk_acc[C::DB], dv_acc[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) {
+    dk_acc[db] = f32x16{};
+    dv_acc[db] = f32x16{};
+  }
+  constexpr float kL2e = kLog2e;
+
+  if (t_first < nt) copies(t_first, qr0, qt0, dr0, dt0, ls0, de0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  // Tile t (query rows q0 .. q0+63): start the copies of tile t+1, then
+  // S, dP, P, dS and the two products for this wave's 32 keys.
+  auto step = [&](const int t, const lds_u8* qr, const lds_u8* qt, const lds_u8* dr,
+                  const lds_u8* dt, const lds_u8* ls, const lds_u8* de, lds_u8* nqr,
+                  lds_u8* nqt, lds_u8* ndr, lds_u8* ndt, lds_u8* nls, lds_u8* nde) {
+    if (t + 1 < nt) copies(t + 1, nqr, nqt, ndr, ndt, nls, nde);
+    const int q0 = t * 64;
+    // causal: this wave's keys are seen only by queries >= kw0
+    if (kw0 < S && (!CAUSAL || q0 + 63 >= kw0)) {
+      f32x16 s[C::KB], dp[C::KB];
+      qk_tile<C>(s, qr, kf, k_off);    // S[q][key]  (rows: queries, lane: key)
+      qk_tile<C>(dp, dr, vf, k_off);   // dP[q][key]
+      const bool masked = (CAUSAL && q0 < kw0 + 31) || (q0 + 64 > S);
+      bf16x8 pq[C::PCH], dsq[C::PCH];
+#pragma unroll
+      for (int qb = 0; qb < C::KB; ++qb) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          // register r = 8*half + e holds query row 32*qb + 16*half + 8*hh + e
+          const int rb = 32 * qb + 16 * half + 8 * hh;
+          float lse8[8], del8[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            lse8[e] = reinterpret_cast<const lds_f32*>(ls)[rb + e];
+            del8[e] = reinterpret_cast<const lds_f32*>(de)[rb + e];
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int r = 8 * half + e;
+            float p = fast_exp2(fmaf(s[qb][r], c, -lse8[e] * kL2e));
+            if (masked) {
+              const int q = q0 + rb + e;
+              if (q >= S || (CAUSAL && my_k > q)) p = 0.0f;
+            }
+            const float ds = p * (dp[qb][r] - del8[e]);
+            pq[2 * qb + half][e] = (__bf16)p;
+            dsq[2 * qb + half][e] = (__bf16)ds;
+          }
+        }
+      }
+      tr_product<C>(dv_acc, dt, pq, v_off);   // dV^T += dO^T P
+      tr_product<C>(dk_acc, qt, dsq, v_off);  // dK^T += q^T dS
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+  int t = t_first;
+  for (; t + 1 < nt; t += 2) {
+    step(t, qr0, qt0, dr0, dt0, ls0, de0, qr1, qt1, dr1, dt1, ls1, de1);
+    step(t + 1, qr1, qt1, dr1, dt1, ls1, de1, qr0, qt0, dr0, dt0, ls0, de0);
+  }
+  if (t < nt) step(t, qr0, qt0, dr0, dt0, ls0, de0, qr1, qt1, dr1, dt1, ls1, de1);
+
+  if (my_k >= S) return;
+  store_col<C::DB>(dK + head + (size_t)my_k * D, dk_acc, scale, hh);
+  store_col<C::DB>(dV + head + (size_t)my_k * D, dv_acc, 1.0f, hh);
+}
+
+// ----------------------------------------------------------------------------
+// dQ: one workgroup per (128 queries, head, batch)
+// ----------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void fa_bwd_dq_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+    const float* __restrict__ LSE, const float* __restrict__ Delta, uint16_t* __restrict__ dQ,
+    int S, int nq, int bh_total, int group_heads, float c, float scale) {
+  using C = BfCfg<D, 64, 4>;  // key tiles of 64; 4 waves of 32 queries
+  // K tile in two layouts (row reads for S^T, transposed reads for dq), V
+  // tile row-wise (for dP^T); two stages.
+  __shared__ __attribute__((aligned(1024))) uint8_t kr0_raw[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t kr1_raw[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t kt0_raw[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t kt1_raw[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vr0_raw[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vr1_raw[C::TILE_BYTES];
+  lds_u8* kr0 = (lds_u8*)kr0_raw;
+  lds_u8* kr1 = (lds_u8*)kr1_raw;
+  lds_u8* kt0 = (lds_u8*)kt0_raw;
+  lds_u8* kt1 = (lds_u8*)kt1_raw;
+  lds_u8* vr0 = (lds_u8*)vr0_raw;
+  lds_u8* vr1 = (lds_u8*)vr1_raw;
+
+  int bh, qt;
+  decode_tile<CAUSAL>(xcd_logical_index(blockIdx.x, nq * bh_total), nq, bh_total, group_heads,
+                      bh, qt);
+  const size_t head = (size_t)bh * (size_t)S * D;
+  const uint16_t* Qh = Q + head;
+  const uint16_t* Kh = K + head;
+  const uint16_t* Vh = V + head;
+  const uint16_t* dOh = dO + head;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int m = lane & 31;
+  const int hh = lane >> 5;
+  const int q0 = qt * 128;
+  const int qw0 = q0 + wave * kRowsPerWave;
+  const int my_q = qw0 + m;
+
+  const int kend = CAUSAL ? min(S, q0 + 128) : S;
+  const int ntiles = (kend + 63) / 64;
+  const int wave_klast = CAUSAL ? min(qw0 + kRowsPerWave - 1, S - 1) : (S - 1);
+  const int wave_ntiles = qw0 < S ? min(ntiles, wave_klast / 64 + 1) : 0;
+
+  int koff[C::LOADS_PER_WAVE], krow[C::LOADS_PER_WAVE];
+  int toff[C::LOADS_PER_WAVE], trow[C::LOADS_PER_WAVE];
+  tile_offsets<C, false>(koff, krow, wave, lane);
+  tile_offsets<C, true>(toff, trow, wave, lane);
+  auto copies = [&](int j, lds_u8* kr, lds_u8* ktt, lds_u8* vr) {
+    const int k0 = j * 64;
+    issue_tile<C>(Kh, kr, k0, S, wave, koff, krow);
+    issue_tile<C>(Kh, ktt, k0, S, wave, toff, trow);
+    issue_tile<C>(Vh, vr, k0, S, wave, koff, krow);
+  };
+
+  bf16x8 qf[C::KCH], df[C::KCH];
+  row_fragments<C>(qf, Qh, my_q, S, hh);
+  row_fragments<C>(df, dOh, my_q, S, hh);
+  int k_off[C::NKOFF], v_off[C::NVOFF];
+  operand_offsets<C>(lane, k_off, v_off);
+  const float lse2 = my_q < S ? LSE[(size_t)bh * S + my_q] * kLog2e : 0.0f;
+  const float delta = my_q < S ? Delta[(size_t)bh * S + my_q] : 0.0f;
+
+  f32x16 acc[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
+
+  if (ntiles > 0) copies(0, kr0, kt0, vr0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  auto step = [&](const int j, const lds_u8* kr, const lds_u8* ktt, const lds_u8* vr,
+                  lds_u8* nkr, lds_u8* nkt, lds_u8* nvr) {
+    if (j + 1 < ntiles) copies(j + 1, nkr, nkt, nvr);
+    if (j < wave_ntiles) {
+      const int k0 = j * 64;
+      f32x16 s[C::KB], dp[C::KB];
+      qk_tile<C>(s, kr, qf, k_off);   // S^T[key][q]
+      qk_tile<C>(dp, vr, df, k_off);  // dP^T[key][q]
+      const bool masked = (CAUSAL && (k0 + 63 > qw0)) || (k0 + 64 > S);
+      const int lim = (CAUSAL ? min(my_q, S - 1) : (S - 1)) - k0 - hh * 8;
+      bf16x8 dsf[C::PCH];
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          // register r of block kb holds key kb*32 + (r>>3)*16 + hh*8 + (r&7)
+          float p = fast_exp2(fmaf(s[kb][r], c, -lse2));
+          if (masked && kb * 32 + (r >> 3) * 16 + (r & 7) > lim) p = 0.0f;
+          dsf[2 * kb + (r >> 3)][r & 7] = (__bf16)(p * (dp[kb][r] - delta));
+        }
+      tr_product<C>(acc, ktt, dsf, v_off);  // dq^T += K^T dS^T
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+  int j = 0;
+  for (; j + 1 < ntiles; j += 2) {
+    step(j, kr0, kt0, vr0, kr1, kt1, vr1);
+    step(j + 1, kr1, kt1, vr1, kr0, kt0, vr0);
+  }
+  if (j < ntiles) step(j, kr0, kt0, vr0, kr1, kt1, vr1);
+
+  if (my_q >= S) return;
+  store_col<C::DB>(dQ + head + (size_t)my_q * D, acc, scale, hh);
+}
+
+// ----------------------------------------------------------------------------
+// Host side
+// ----------------------------------------------------------------------------
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+template <class KernelT, class... Args>
+int launch_k(KernelT kernel, unsigned grid, unsigned threads, hipStream_t stream,
+             Args... args) {
+  void* argv[] = {static_cast<void*>(&args)...};
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(grid),
+                                       dim3(threads), argv, 0, stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+template <int D>
+int run_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
+            const uint16_t* dout, const float* lse, uint16_t* dq, uint16_t* dk, uint16_t* dv,
+            float* delta, int bh, int S, bool causal, float scale, hipStream_t s) {
+  const int64_t rows = (int64_t)bh * S;
+  const float c = scale * kLog2e;
+  const int group_heads = bh >= 8 ? bh / 8 : 1;
+  int st = launch_k(fa_bwd_delta_kernel<D>, (unsigned)((rows * (D / 8) + 255) / 256), 256, s,
+                    o, dout, delta, rows);
+  if (st != FA_OK) return st;
+  const int nk = (S + 127) / 128;
+  const unsigned grid = (unsigned)nk * (unsigned)bh;
+  if (causal)
+    st = launch_k(fa_bwd_dkdv_kernel<D, true>, grid, 256, s, q, k, v, dout, (const float*)lse,
+                  (const float*)delta, dk, dv, S, nk, bh, group_heads, c, scale);
+  else
+    st = launch_k(fa_bwd_dkdv_kernel<D, false>, grid, 256, s, q, k, v, dout, (const float*)lse,
+                  (const float*)delta, dk, dv, S, nk, bh, group_heads, c, scale);
+  if (st != FA_OK) return st;
+  if (causal)
+    return launch_k(fa_bwd_dq_kernel<D, true>, grid, 256, s, q, k, v, dout, (const float*)lse,
+                    (const float*)delta, dq, S, nk, bh, group_heads, c, scale);
+  return launch_k(fa_bwd_dq_kernel<D, false>, grid, 256, s, q, k, v, dout, (const float*)lse,
+                  (const float*)delta, dq, S, nk, bh, group_heads, c, scale);
+}
+
+}  // namespace
+
+extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o,
+                      const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                      float* delta, int B, int H, int S, int D, int causal, float scale,
+                      void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !delta) return FA_ERR_NULL;
+  if (B < 1 || H < 1 || S < 1) return FA_ERR_SHAPE;
+  if (D != 64 && D != 128) return FA_ERR_HEADDIM;
+  if (causal != 0 && causal != 1) return FA_ERR_CAUSAL;
+  if (!(scale > 0.0f) || !isfinite(scale)) return FA_ERR_SCALE;
+  const int64_t bh = (int64_t)B * H;
+  const int64_t nk = ((int64_t)S + 127) / 128;
+  if (bh > INT32_MAX || (int64_t)S * D > INT32_MAX || nk * bh > INT32_MAX ||
+      (uint64_t)(bh * S * D) > (uint64_t)(SIZE_MAX / 4))
+    return FA_ERR_SHAPE;
+  const uintptr_t a16 = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o |
+                        (uintptr_t)dout | (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv;
+  if ((a16 & 15u) || (((uintptr_t)lse | (uintptr_t)delta) & 3u)) return FA_ERR_ALIGN;
+  const size_t tb = (size_t)(bh * S * D) * 2, lb = (size_t)(bh * S) * sizeof(float);
+  const void* ins[6] = {q, k, v, o, dout, lse};
+  const size_t in_b[6] = {tb, tb, tb, tb, tb, lb};
+  void* outs[4] = {dq, dk, dv, delta};
+  const size_t out_b[4] = {tb, tb, tb, lb};
+  for (int a = 0; a < 4; ++a) {
+    for (int i = 0; i < 6; ++i)
+      if (overlap(outs[a], out_b[a], ins[i], in_b[i])) return FA_ERR_ALIAS;
+    for (int b = a + 1; b < 4; ++b)
+      if (overlap(outs[a], out_b[a], outs[b], out_b[b])) return FA_ERR_ALIAS;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const auto* Q = static_cast<const uint16_t*>(q);
+  const auto* Kp = static_cast<const uint16_t*>(k);
+  const auto* Vp = static_cast<const uint16_t*>(v);
+  const auto* O = static_cast<const uint16_t*>(o);
+  const auto* dO = static_cast<const uint16_t*>(dout);
+  auto* dQ = static_cast<uint16_t*>(dq);
+  auto* dK = static_cast<uint16_t*>(dk);
+  auto* dV = static_cast<uint16_t*>(dv);
+  if (D == 64)
+    return run_bwd<64>(Q, Kp, Vp, O, dO, lse, dQ, dK, dV, delta, (int)bh, S, causal != 0, scale, s);
+  return run_bwd<128>(Q, Kp, Vp, O, dO, lse, dQ, dK, dV, delta, (int)bh, S, causal != 0, scale, s);
+}

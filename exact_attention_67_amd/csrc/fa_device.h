@@ -1,0 +1,216 @@
+// Device-side building blocks shared by the attention kernels of this library
+// (forward: fa_fwd.hip; backward: fa_bwd.hip): vector types, the gfx950 MFMA
+// operand layouts used by both, LDS swizzles, the asynchronous global -> LDS
+// tile copy, the S tile product and the XCD-aware grid decode.
+//
+// MFMA layout (v_mfma_f32_32x32x16_bf16, wave64): A operand -- lane l holds
+// A[l % 32][8 * (l / 32) + e], e = 0..7; B operand -- lane l holds
+// B[8 * (l / 32) + e][l % 32]; accumulator -- lane l, register r holds
+// C[(r / 4) * 8 + (l / 32) * 4 + r % 4][l % 32].  A lane therefore owns one
+// column of C.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
+
+constexpr int kRowsPerWave = 32;  // query (or key) rows per wavefront
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ float other_half(float x) {
+  // value held by lane l ^ 32 (the other 32-lane half of the wavefront)
+  return __shfl_xor(x, 32);
+}
+
+// Logical workgroup index from the hardware one: workgroup i is dispatched to
+// XCD i % 8; give each XCD a contiguous range of logical indices.
+__device__ __forceinline__ int xcd_logical_index(int i, int n) {
+  const int x = i & 7, s = i >> 3;
+  const int base = n >> 3, rem = n & 7;
+  return x * base + (x < rem ? x : rem) + s;
+}
+
+// Logical index -> (bh, query tile).  Heads are taken in groups of
+// `group_heads`; inside a group the tiles of its heads are interleaved, and
+// when causal the heaviest (last) query tiles come first.
+template <bool CAUSAL>
+__device__ __forceinline__ void decode_tile(int L, int nq, int bh_total, int group_heads,
+                                            int& bh, int& qt) {
+  const int gsize = group_heads * nq;
+  const int grp = L / gsize;
+  const int r = L - grp * gsize;
+  const int left = bh_total - grp * group_heads;
+  const int hin = left < group_heads ? left : group_heads;
+  bh = grp * group_heads + r % hin;
+  const int rank = r / hin;
+  qt = CAUSAL ? (nq - 1 - rank) : rank;
+}
+
+// ----------------------------------------------------------------------------
+// bf16 kernel
+// ----------------------------------------------------------------------------
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+
+// A row's reference max is only raised when its running max exceeds it by
+// more than this many powers of two, so softmax weights stay <= 2^8.
+constexpr float kRescaleThreshold = 8.0f;
+
+template <int D_, int BC_, int WAVES_>
+struct BfCfg {
+  static constexpr int D = D_;
+  static constexpr int BC = BC_;                       // keys per tile
+  static constexpr int WAVES = WAVES_;                 // wavefronts per workgroup
+  static constexpr int BR = kRowsPerWave * WAVES;      // query rows per workgroup
+  static constexpr int KCH = D / 16;                   // MFMA k-steps of Q*K^T
+  static constexpr int KB = BC / 32;                   // 32-key blocks per tile
+  static constexpr int DB = D / 32;                    // 32-row blocks of O^T
+  static constexpr int PCH = BC / 16;                  // MFMA k-steps of P*V
+  static constexpr int ROW_BYTES = D * 2;              // one K or V row in LDS
+  static constexpr int TILE_BYTES = BC * ROW_BYTES;    // K tile or V tile
+  static constexpr int LDS_BYTES = 4 * TILE_BYTES;     // 2 K + 2 V buffers
+  static constexpr int RC = D / 8;                     // 16-byte chunks per row
+  static constexpr int ROWS_PER_LOAD = 64 / RC;        // rows per 1 KiB wave load
+  // Waves that issue the tile copies: all of a 4-wave workgroup; in an 8-wave
+  // workgroup only waves 0..3 (one per SIMD), which leaves their SIMD
+  // partners free to start on the matrix cores right after the barrier.
+  static constexpr int COPY_WAVES = WAVES == 8 ? 4 : WAVES;
+  static constexpr int LOADS_PER_WAVE = TILE_BYTES / 1024 / COPY_WAVES;  // per tensor
+  // VALU instructions the schedule places after each MFMA of a tile.
+  static constexpr int VALU_PER_MFMA = WAVES == 8 ? 4 : 5;
+  // LDS bank geometry: 64 banks of 4 bytes, i.e. 256-byte bank lines.
+  static constexpr int ROWS_PER_LINE = 256 / ROW_BYTES > 1 ? 256 / ROW_BYTES : 1;
+  static constexpr int CH_PER_LINE = 16;               // 16-byte chunks per bank line
+  static constexpr int NKOFF = KCH < 8 ? KCH : 8;      // distinct K read offsets
+  static constexpr int NVOFF = DB < 4 ? DB : 4;        // distinct V read offsets
+  static_assert(TILE_BYTES % (1024 * COPY_WAVES) == 0, "tile must split into 1 KiB wave loads");
+  static_assert(COPY_WAVES * LOADS_PER_WAVE * 1024 == TILE_BYTES, "copy shares cover the tile");
+  static_assert(COPY_WAVES * LOADS_PER_WAVE * ROWS_PER_LOAD == BC, "copy rows stay in the tile");
+  static_assert(D % 32 == 0 && BC % 32 == 0 && D >= 64 && RC <= 64, "tile shape");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+};
+
+// 16-byte chunk swizzles (physical chunk = logical chunk ^ swizzle(row)), for
+// an LDS of 64 four-byte banks (a 16-lane group of 16-byte reads, or a
+// 32-lane group of 8-byte reads, is served per pass).
+// K: a 16-lane group reads one chunk column of 16 different rows of a 32-row
+// block -> the 16 rows of a bank line's worth must land in 16 distinct chunk
+// slots: XOR with the row index among the rows that share a line position.
+template <class C>
+__device__ __forceinline__ int kswz(int r) {
+  return (r / C::ROWS_PER_LINE) & (C::CH_PER_LINE / C::ROWS_PER_LINE - 1);
+}
+// V: a 32-lane pass of the transposing read covers 4 consecutive rows x 64
+// bytes (4 chunks): shift each row's 4-chunk group to its own slot.
+template <class C>
+__device__ __forceinline__ int vswz(int r) {
+  constexpr int groups = (C::CH_PER_LINE / C::ROWS_PER_LINE) / 4;  // 4-chunk slots per row
+  return ((r / C::ROWS_PER_LINE) & (groups - 1)) << 2;
+}
+
+// MFMA row m of a 32-key block reads key row perm(m): bits 2 and 3 swapped.
+__device__ __forceinline__ int key_perm(int m) {
+  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+
+// The value held by lane l ^ 32, through the gfx950 lane-half swap.
+__device__ __forceinline__ float swap_halves(float x, int hh) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                                  __builtin_bit_cast(unsigned, x), false, false);
+  return __builtin_bit_cast(float, hh ? r[0] : r[1]);
+}
+
+// Per-lane element offsets (within one head, tile starting at key 0) of the
+// 16-byte pieces this lane copies; row r of the tile lands in LDS row r with
+// its chunks swizzled.
+template <class C, bool IS_V>
+__device__ __forceinline__ void tile_offsets(int* off, int* row, int part, int lane) {
+#pragma unroll
+  for (int u = 0; u < C::LOADS_PER_WAVE; ++u) {
+    const int n = part * C::LOADS_PER_WAVE + u;
+    const int r = n * C::ROWS_PER_LOAD + lane / C::RC;
+    const int lch = (lane % C::RC) ^ (IS_V ? vswz<C>(r) : kswz<C>(r));
+    row[u] = r;
+    off[u] = r * C::D + lch * 8;
+  }
+}
+
+// Asynchronous global -> LDS copy of one K or V tile.  Share `part` of the
+// copy, issued by one wave, is LOADS_PER_WAVE transfers of 1 KiB, lane l
+// filling bytes 16l .. 16l+15 (a wave-uniform base address plus a per-lane
+// 32-bit offset).  In the last (partial) tile, rows past the sequence end are
+// clamped to the last row: finite data whose keys are masked.
+template <class C>
+__device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ head_src, lds_u8* dst,
+                                           int k0, int S, int part, const int* off,
+                                           const int* row) {
+  // The tile's base address is wave-uniform: keep it in scalar registers so
+  // each copy is issued as scalar base + 32-bit lane offset.
+  const uint64_t b64 = (uint64_t)(head_src + (size_t)k0 * C::D);
+  const uint32_t b_lo = __builtin_amdgcn_readfirstlane((uint32_t)b64);
+  const uint32_t b_hi = __builtin_amdgcn_readfirstlane((uint32_t)(b64 >> 32));
+  const char* base = (const char*)(((uint64_t)b_hi << 32) | b_lo);
+  lds_u8* lds = dst + part * (C::LOADS_PER_WAVE * 1024);
+  if (k0 + C::BC <= S) {
+#pragma unroll
+    for (int u = 0; u < C::LOADS_PER_WAVE; ++u) {
+      const void* gp = base + (uint32_t)(off[u] * 2);
+      lds_u8* lp = lds + u * 1024;
+      __builtin_amdgcn_global_load_lds(gp, lp, 16, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < C::LOADS_PER_WAVE; ++u) {
+      const int o = off[u] - (row[u] - min(row[u], S - 1 - k0)) * C::D;
+      const void* gp = base + (uint32_t)(o * 2);
+      lds_u8* lp = lds + u * 1024;
+      __builtin_amdgcn_global_load_lds(gp, lp, 16, 0, 0);
+    }
+  }
+}
+
+// S^T (keys x queries) for one tile: s[kb] = K[kb*32 + perm(m)][:] . Q[my_q][:]
+template <class C>
+__device__ __forceinline__ void qk_tile(f32x16 (&s)[C::KB], const lds_u8* Ks,
+                                        const bf16x8 (&qf)[C::KCH], const int (&k_off)[C::NKOFF]) {
+#pragma unroll
+  for (int kb = 0; kb < C::KB; ++kb) {
+#pragma unroll
+    for (int ch = 0; ch < C::KCH; ++ch) {
+      const bf16x8 kf = *(const lds_bf16x8*)(Ks + kb * 32 * C::ROW_BYTES +
+                                              (ch / C::NKOFF) * 256 + k_off[ch % C::NKOFF]);
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ch], ch == 0 ? f32x16{} : s[kb], 0,
+                                                      0, 0);
+    }
+  }
+}
+
+// Row max of a tile's raw scores for the lane's query (both lane halves).
+template <class C>
+__device__ __forceinline__ float row_max(const f32x16 (&s)[C::KB], int hh) {
+  float x = s[0][0];
+#pragma unroll
+  for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x = fmaxf(x, s[kb][r]);
+  return fmaxf(x, swap_halves(x, hh));
+}
+
+}  // namespace

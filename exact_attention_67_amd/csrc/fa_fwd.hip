@@ -1,9 +1,9 @@
 // Fused, tiled, exact attention forward for MI355X (gfx950, CDNA4).
 //
-// One workgroup of 4 wavefronts owns one (query tile of 128 rows, head,
-// batch); each wavefront owns 32 query rows.  Key/value tiles are streamed
-// through LDS with a running (online) softmax, so the seq x seq score matrix
-// only ever exists in registers -- the method of "Profiling in PyTorch
+// One workgroup of 4 or 8 wavefronts owns one (query tile of 128 or 256 rows,
+// head, batch); each wavefront owns 32 query rows.  Key/value tiles are
+// streamed through LDS with a running (online) softmax, so the seq x seq score
+// matrix only ever exists in registers -- the method of "Profiling in PyTorch
 // (Part 3): Attention is all you profile", section "Why flash attention
 // exists", with the FlashAttention-2 choices listed in the "FlashAttention-2"
 // blog, section "FlashAttention-2 Optimizations": causal tiles that are fully
@@ -11,9 +11,9 @@
 // heads, and the work is split between waves by query rows so that no
 // cross-wave reduction is needed.  The "Pipelining GmemCopy on kHeadDim" issue
 // discusses overlapping the global-memory copy of the next key block with the
-// math on the current one; here the next K/V tile is fetched into registers
-// while the current one is consumed from the other half of a double-buffered
-// LDS stage.
+// math on the current one; here whole K/V tiles are copied one to two tiles
+// ahead, straight from global memory into LDS (no register staging), into
+// double-buffered (a four-deep ring at D = 256) LDS buffers.
 //
 // gfx950 mapping (bf16 path):
 //  * Both contractions run on v_mfma_f32_32x32x16_bf16 in transposed form:
@@ -22,22 +22,25 @@
 //    so a query's row max / row sum is an in-lane reduction plus one exchange
 //    between lane l and lane l^32, and the per-query rescale factor multiplies
 //    the lane's own O^T column.
-//  * The 32 K rows fed to one MFMA are loaded in a permuted order (bits 2 and 3
-//    of the row index swapped).  With that order the first 8 accumulator
-//    registers of a lane hold 8 consecutive keys, so after the softmax a
-//    lane's registers are directly the B operand of the P*V MFMA.
-//  * V is transposed in registers on its way into LDS (key-contiguous rows),
-//    so the A operand of O^T = V^T * P^T is one 16-byte LDS read per lane.
-//  * LDS rows are XOR-swizzled in 16-byte units so the MFMA operand reads and
-//    the staging writes are free of bank conflicts.
-//  * exp2 with the scale folded into one FMA per score.  The rescale of the
-//    O accumulator is skipped (wave-uniform branch) on tiles where no row's
-//    running max grows, which is most tiles of a long sequence.  The reference
-//    max always equals the running max, so a row's largest weight is exactly
-//    1 and rounds to bf16 without error.
+//  * The 32 K rows fed to one MFMA are read in a permuted order (bits 2 and 3
+//    of the row index swapped).  With that order a lane's accumulator
+//    registers hold runs of 8 consecutive keys, so after the softmax they are
+//    directly the B operand of the P*V MFMA.
+//  * V stays row-major in LDS; the V^T operand is read with the transposing
+//    LDS read (two ds_read_b64_tr_b16 per MFMA).
+//  * LDS rows are XOR-swizzled in 16-byte units so the MFMA operand reads are
+//    free of bank conflicts on the 64-bank LDS.
+//  * exp2 with the scale folded into one FMA per score.  The reference max of
+//    a row is raised only when the row's max exceeds it by more than 2^8, so
+//    the rescale of the O accumulator (a wave-uniform branch) runs on few
+//    tiles; weights stay <= 2^8, and O is normalised by the sum of the bf16
+//    weights that multiplied V.
 //  * The 1-D grid is decoded XCD-aware (the 8 XCDs receive workgroups round-
 //    robin; consecutive logical tiles of the same heads are kept on one XCD so
 //    they share its L2) and, when causal, heaviest query tiles first.
+//  * Queries against a longer or shorter key sequence (Sq != Sk, causal mask
+//    aligned bottom-right) run through the same kernels; rows with no visible
+//    key give O = 0 and LSE = -inf.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -45,207 +48,13 @@
 #include <stdint.h>
 
 #include "fa.h"
+#include "fa_device.h"
 
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-constexpr float kLn2 = 0.69314718055994530942f;
-constexpr float kLog2e = 1.44269504088896340736f;
-
-constexpr int kWaves = 4;
+constexpr int kWaves = 4;                   // float32 kernel: wavefronts per workgroup
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRowsPerWave = 32;
-constexpr int kBr = kRowsPerWave * kWaves;  // query rows per workgroup
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
-
-__device__ __forceinline__ float other_half(float x) {
-  // value held by lane l ^ 32 (the other 32-lane half of the wavefront)
-  return __shfl_xor(x, 32);
-}
-
-// Logical workgroup index from the hardware one: workgroup i is dispatched to
-// XCD i % 8; give each XCD a contiguous range of logical indices.
-__device__ __forceinline__ int xcd_logical_index(int i, int n) {
-  const int x = i & 7, s = i >> 3;
-  const int base = n >> 3, rem = n & 7;
-  return x * base + (x < rem ? x : rem) + s;
-}
-
-// Logical index -> (bh, query tile).  Heads are taken in groups of
-// `group_heads`; inside a group the tiles of its heads are interleaved, and
-// when causal the heaviest (last) query tiles come first.
-template <bool CAUSAL>
-__device__ __forceinline__ void decode_tile(int L, int nq, int bh_total, int group_heads,
-                                            int& bh, int& qt) {
-  const int gsize = group_heads * nq;
-  const int grp = L / gsize;
-  const int r = L - grp * gsize;
-  const int left = bh_total - grp * group_heads;
-  const int hin = left < group_heads ? left : group_heads;
-  bh = grp * group_heads + r % hin;
-  const int rank = r / hin;
-  qt = CAUSAL ? (nq - 1 - rank) : rank;
-}
-
-// ----------------------------------------------------------------------------
-// bf16 kernel
-// ----------------------------------------------------------------------------
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) uint8_t lds_u8;
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
-
-// A row's reference max is only raised when its running max exceeds it by
-// more than this many powers of two, so softmax weights stay <= 2^8.
-constexpr float kRescaleThreshold = 8.0f;
-
-template <int D_, int BC_, int WAVES_>
-struct BfCfg {
-  static constexpr int D = D_;
-  static constexpr int BC = BC_;                       // keys per tile
-  static constexpr int WAVES = WAVES_;                 // wavefronts per workgroup
-  static constexpr int BR = kRowsPerWave * WAVES;      // query rows per workgroup
-  static constexpr int KCH = D / 16;                   // MFMA k-steps of Q*K^T
-  static constexpr int KB = BC / 32;                   // 32-key blocks per tile
-  static constexpr int DB = D / 32;                    // 32-row blocks of O^T
-  static constexpr int PCH = BC / 16;                  // MFMA k-steps of P*V
-  static constexpr int ROW_BYTES = D * 2;              // one K or V row in LDS
-  static constexpr int TILE_BYTES = BC * ROW_BYTES;    // K tile or V tile
-  static constexpr int LDS_BYTES = 4 * TILE_BYTES;     // 2 K + 2 V buffers
-  static constexpr int RC = D / 8;                     // 16-byte chunks per row
-  static constexpr int ROWS_PER_LOAD = 64 / RC;        // rows per 1 KiB wave load
-  // Waves that issue the tile copies: all of a 4-wave workgroup; in an 8-wave
-  // workgroup only waves 0..3 (one per SIMD), which leaves their SIMD
-  // partners free to start on the matrix cores right after the barrier.
-  static constexpr int COPY_WAVES = WAVES == 8 ? 4 : WAVES;
-  static constexpr int LOADS_PER_WAVE = TILE_BYTES / 1024 / COPY_WAVES;  // per tensor
-  // VALU instructions the schedule places after each MFMA of a tile.
-  static constexpr int VALU_PER_MFMA = WAVES == 8 ? 4 : 5;
-  // LDS bank geometry: 64 banks of 4 bytes, i.e. 256-byte bank lines.
-  static constexpr int ROWS_PER_LINE = 256 / ROW_BYTES > 1 ? 256 / ROW_BYTES : 1;
-  static constexpr int CH_PER_LINE = 16;               // 16-byte chunks per bank line
-  static constexpr int NKOFF = KCH < 8 ? KCH : 8;      // distinct K read offsets
-  static constexpr int NVOFF = DB < 4 ? DB : 4;        // distinct V read offsets
-  static_assert(TILE_BYTES % (1024 * COPY_WAVES) == 0, "tile must split into 1 KiB wave loads");
-  static_assert(COPY_WAVES * LOADS_PER_WAVE * 1024 == TILE_BYTES, "copy shares cover the tile");
-  static_assert(COPY_WAVES * LOADS_PER_WAVE * ROWS_PER_LOAD == BC, "copy rows stay in the tile");
-  static_assert(D % 32 == 0 && BC % 32 == 0 && D >= 64 && RC <= 64, "tile shape");
-  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
-};
-
-// 16-byte chunk swizzles (physical chunk = logical chunk ^ swizzle(row)), for
-// an LDS of 64 four-byte banks (a 16-lane group of 16-byte reads, or a
-// 32-lane group of 8-byte reads, is served per pass).
-// K: a 16-lane group reads one chunk column of 16 different rows of a 32-row
-// block -> the 16 rows of a bank line's worth must land in 16 distinct chunk
-// slots: XOR with the row index among the rows that share a line position.
-template <class C>
-__device__ __forceinline__ int kswz(int r) {
-  return (r / C::ROWS_PER_LINE) & (C::CH_PER_LINE / C::ROWS_PER_LINE - 1);
-}
-// V: a 32-lane pass of the transposing read covers 4 consecutive rows x 64
-// bytes (4 chunks): shift each row's 4-chunk group to its own slot.
-template <class C>
-__device__ __forceinline__ int vswz(int r) {
-  constexpr int groups = (C::CH_PER_LINE / C::ROWS_PER_LINE) / 4;  // 4-chunk slots per row
-  return ((r / C::ROWS_PER_LINE) & (groups - 1)) << 2;
-}
-
-// MFMA row m of a 32-key block reads key row perm(m): bits 2 and 3 swapped.
-__device__ __forceinline__ int key_perm(int m) {
-  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
-}
-
-// The value held by lane l ^ 32, through the gfx950 lane-half swap.
-__device__ __forceinline__ float swap_halves(float x, int hh) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
-                                                  __builtin_bit_cast(unsigned, x), false, false);
-  return __builtin_bit_cast(float, hh ? r[0] : r[1]);
-}
-
-// Per-lane element offsets (within one head, tile starting at key 0) of the
-// 16-byte pieces this lane copies; row r of the tile lands in LDS row r with
-// its chunks swizzled.
-template <class C, bool IS_V>
-__device__ __forceinline__ void tile_offsets(int* off, int* row, int part, int lane) {
-#pragma unroll
-  for (int u = 0; u < C::LOADS_PER_WAVE; ++u) {
-    const int n = part * C::LOADS_PER_WAVE + u;
-    const int r = n * C::ROWS_PER_LOAD + lane / C::RC;
-    const int lch = (lane % C::RC) ^ (IS_V ? vswz<C>(r) : kswz<C>(r));
-    row[u] = r;
-    off[u] = r * C::D + lch * 8;
-  }
-}
-
-// Asynchronous global -> LDS copy of one K or V tile.  Share `part` of the
-// copy, issued by one wave, is LOADS_PER_WAVE transfers of 1 KiB, lane l
-// filling bytes 16l .. 16l+15 (a wave-uniform base address plus a per-lane
-// 32-bit offset).  In the last (partial) tile, rows past the sequence end are
-// clamped to the last row: finite data whose keys are masked.
-template <class C>
-__device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ head_src, lds_u8* dst,
-                                           int k0, int S, int part, const int* off,
-                                           const int* row) {
-  // The tile's base address is wave-uniform: keep it in scalar registers so
-  // each copy is issued as scalar base + 32-bit lane offset.
-  const uint64_t b64 = (uint64_t)(head_src + (size_t)k0 * C::D);
-  const uint32_t b_lo = __builtin_amdgcn_readfirstlane((uint32_t)b64);
-  const uint32_t b_hi = __builtin_amdgcn_readfirstlane((uint32_t)(b64 >> 32));
-  const char* base = (const char*)(((uint64_t)b_hi << 32) | b_lo);
-  lds_u8* lds = dst + part * (C::LOADS_PER_WAVE * 1024);
-  if (k0 + C::BC <= S) {
-#pragma unroll
-    for (int u = 0; u < C::LOADS_PER_WAVE; ++u) {
-      const void* gp = base + (uint32_t)(off[u] * 2);
-      lds_u8* lp = lds + u * 1024;
-      __builtin_amdgcn_global_load_lds(gp, lp, 16, 0, 0);
-    }
-  } else {
-#pragma unroll
-    for (int u = 0; u < C::LOADS_PER_WAVE; ++u) {
-      const int o = off[u] - (row[u] - min(row[u], S - 1 - k0)) * C::D;
-      const void* gp = base + (uint32_t)(o * 2);
-      lds_u8* lp = lds + u * 1024;
-      __builtin_amdgcn_global_load_lds(gp, lp, 16, 0, 0);
-    }
-  }
-}
-
-// S^T (keys x queries) for one tile: s[kb] = K[kb*32 + perm(m)][:] . Q[my_q][:]
-template <class C>
-__device__ __forceinline__ void qk_tile(f32x16 (&s)[C::KB], const lds_u8* Ks,
-                                        const bf16x8 (&qf)[C::KCH], const int (&k_off)[C::NKOFF]) {
-#pragma unroll
-  for (int kb = 0; kb < C::KB; ++kb) {
-#pragma unroll
-    for (int ch = 0; ch < C::KCH; ++ch) {
-      const bf16x8 kf = *(const lds_bf16x8*)(Ks + kb * 32 * C::ROW_BYTES +
-                                              (ch / C::NKOFF) * 256 + k_off[ch % C::NKOFF]);
-      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ch], ch == 0 ? f32x16{} : s[kb], 0,
-                                                      0, 0);
-    }
-  }
-}
-
-// Row max of a tile's raw scores for the lane's query (both lane halves).
-template <class C>
-__device__ __forceinline__ float row_max(const f32x16 (&s)[C::KB], int hh) {
-  float x = s[0][0];
-#pragma unroll
-  for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) x = fmaxf(x, s[kb][r]);
-  return fmaxf(x, swap_halves(x, hh));
-}
+constexpr int kBr = kRowsPerWave * kWaves;  // float32 kernel: query rows per workgroup
 
 // Two waves per SIMD up to D = 128 (two 4-wave or one 8-wave workgroup per
 // CU); D = 256 needs the full register file.

@@ -132,6 +132,33 @@ int fa_merge(const void* o_parts, const float* lse_parts, int G, int B, int H, i
              void* o, float* lse, void* stream);
 
 /*
+ * fa_bwd -- bf16 attention backward: gradients of the fa_fwd output with
+ * respect to q, k and v, for an incoming gradient dout of o.
+ *   q, k, v : bf16 [B,H,S,D] inputs of the forward call (device).
+ *   o, lse  : that call's outputs (bf16 [B,H,S,D], float32 [B,H,S]).
+ *   dout    : bf16 [B,H,S,D] gradient of the loss with respect to o.
+ *   dq, dk, dv : bf16 [B,H,S,D] results (device), fully overwritten.
+ *   delta   : float32 [B,H,S] buffer owned by the caller, overwritten with
+ *             rowsum(dout * o) (an intermediate the kernels share; it is an
+ *             output so that the call itself allocates nothing).
+ *   D       : 64 or 128.
+ *   B, H, S, causal, scale, stream : as for fa_fwd (same values as the
+ *             forward call).
+ * Computes, with P = exp(scale * q k^T - lse) (masked entries 0):
+ *   dv = P^T dout;  dS = P * (dout v^T - delta);  dq = scale * dS k;
+ *   dk = scale * dS^T q
+ * -- the gradient of the operation described for fa_fwd, which the pages
+ * describe only in its forward direction.  bf16 products with float32
+ * accumulation; P and dS are rounded to bf16 (nearest even) before the
+ * products they feed.  Alignment: pointers to bf16 tensors 16-byte aligned,
+ * lse and delta 4-byte aligned.  dq, dk, dv and delta must not overlap each
+ * other or any input.  Errors: as for fa_fwd (FA_ERR_HEADDIM for D = 256).
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv, float* delta,
+           int B, int H, int S, int D, int causal, float scale, void* stream);
+
+/*
  * fa_fwd_plan -- the launch shape fa_fwd (elem_bytes = 2) or fa_fwd_f32
  * (elem_bytes = 4) uses for this problem, computed on the host without any
  * HIP call (callable without a GPU).  One workgroup processes one tile of

@@ -135,6 +135,34 @@ def test_merge_validation_errors():
     assert call_merge(o=O, lse=O + 64) == fa.FA_ERR_ALIAS       # outputs overlap
 
 
+def call_bwd(**kw):
+    base = dict(q=Q, k=K, v=V, o=O, do=L, lse=A * 6, dq=A * 7, dk=A * 8, dv=A * 9, delta=A * 10,
+                B=1, H=2, S=100, D=128, causal=1, scale=0.125)
+    base.update(kw)
+    b = base
+    return fa.fa_bwd(b["q"], b["k"], b["v"], b["o"], b["do"], b["lse"], b["dq"], b["dk"],
+                     b["dv"], b["delta"], b["B"], b["H"], b["S"], b["D"], b["causal"],
+                     b["scale"], None)
+
+
+def test_bwd_validation_errors():
+    for name in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv", "delta"):
+        assert call_bwd(**{name: 0}) == fa.FA_ERR_NULL, name
+    for bad in ({"B": 0}, {"S": 0}, {"H": -2}):
+        assert call_bwd(**bad) == fa.FA_ERR_SHAPE, bad
+    for d in (32, 96, 256):
+        assert call_bwd(D=d) == fa.FA_ERR_HEADDIM, d
+    assert call_bwd(causal=5) == fa.FA_ERR_CAUSAL
+    assert call_bwd(scale=0.0) == fa.FA_ERR_SCALE
+    assert call_bwd(dk=A * 8 + 8) == fa.FA_ERR_ALIGN
+    assert call_bwd(delta=A * 10 + 2) == fa.FA_ERR_ALIGN
+    nb = 1 * 2 * 100 * 128 * 2
+    assert call_bwd(dq=Q + nb - 16) == fa.FA_ERR_ALIAS        # dq overlaps q
+    assert call_bwd(dv=A * 7 + 16) == fa.FA_ERR_ALIAS         # dv overlaps dq
+    assert call_bwd(delta=A * 6) == fa.FA_ERR_ALIAS           # delta overlaps lse
+    assert call_bwd(dq=Q + nb, causal=3) == fa.FA_ERR_CAUSAL  # adjacent: no alias
+
+
 def test_forward_rejects_cpu_tensors():
     import torch
     q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
