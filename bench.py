@@ -181,6 +181,32 @@ def time_secondary(steps):
         log(f"[bench] {name}: {avg:.4f} ms, {out[name]['tflops']} TFLOP/s, "
             f"K/V read {out[name]['kv_read_gbs']} GB/s")
         del q, k, v, o, lse
+    for name in ("c3_bf16_2x16x4096x128", "c4_bf16_causal_1x32x16384x128"):
+        w = wl.WORKLOADS[name]
+        q, k, v = (t.cuda() for t in wl.make_inputs(w))
+        g = torch.Generator("cpu").manual_seed(w.seed + 100)
+        do = torch.randn(q.shape, generator=g).to(torch.bfloat16).cuda()
+        o, lse = fa.forward(q, k, v, causal=True, scale=w.scale)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        delta = torch.empty_like(lse)
+        stream = torch.cuda.current_stream().cuda_stream
+        args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+                w.B, w.H, w.S, w.D, 1, w.scale, stream)
+
+        def call():
+            st = fa.fa_bwd(*args)
+            if st != fa.FA_OK:
+                raise fa.FAError(st, "fa_bwd")
+
+        avg, med, mn = _time_launches(call, max(3, steps // 2), 2)
+        flops = 2.5 * w.flops(True)   # five products: S, dP, dV, dK, dQ (nominal)
+        key = "backward_" + name
+        out[key] = {"launch_ms_avg": round(avg, 5), "launch_ms_median": round(med, 5),
+                    "tflops": round(flops / (avg * 1e-3) / 1e12, 2), "causal": True,
+                    "flops_per_launch": flops}
+        log(f"[bench] {key}: {avg:.4f} ms, {out[key]['tflops']} TFLOP/s (2.5x forward flops)")
+        del q, k, v, do, o, lse, dq, dk, dv, delta
     for name, w in wl.MERGE_WORKLOADS.items():
         op, lp = (t.cuda() for t in wl.make_merge_inputs(w))
         o = torch.empty(op.shape[1:], dtype=torch.bfloat16, device="cuda")
