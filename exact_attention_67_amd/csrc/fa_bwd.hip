@@ -23,9 +23,15 @@
 //    queries and keys exchanged), so P and dS are per-lane columns; dV += P^T dO
 //    and dK += dS^T q read dO and q with the transposing LDS read.  q and dO
 //    are each needed both row-wise and transposed, so each query tile is
-//    copied into LDS twice, once per swizzle.
-//  * fa_bwd_dq_kernel: the forward's layout (one query per lane): S^T = K q^T,
-//    dP^T = V dO^T, dS^T, then dq^T += K^T dS^T with K read transposed.
+//    copied into LDS twice, once per swizzle.  Its registers (about 480 per
+//    lane) allow one wavefront per SIMD, so each wave overlaps its own work:
+//    S and dP of the next query tile are computed while the weights and dS
+//    of the current one form.
+//  * fa_bwd_dq_kernel: one workgroup of 8 wavefronts per (block of 256
+//    queries, head, batch), two wavefronts per SIMD as in the forward; waves
+//    0-3 issue the tile copies.  The forward's layout (one query per lane):
+//    S^T = K q^T, dP^T = V dO^T, dS^T, then dq^T += K^T dS^T with K read
+//    transposed.
 // No atomics and no workspace beyond the caller's Delta buffer: dq is
 // accumulated by the workgroup that owns the query tile.
 
@@ -150,9 +156,43 @@ __device__ __forceinline__ void row_fragments(bf16x8 (&f)[C::KCH], const uint16_
   }
 }
 
+// One 32-row block of S = X * frag^T (rows of the tile X, read in the
+// permuted order, against the lane's own fragment): s = X[kb*32 + perm(m)] . frag.
+template <class C>
+__device__ __forceinline__ void qk_block(f32x16& s, const lds_u8* X, const bf16x8 (&f)[C::KCH],
+                                         const int (&k_off)[C::NKOFF], int kb) {
+#pragma unroll
+  for (int ch = 0; ch < C::KCH; ++ch) {
+    const bf16x8 xf = *(const lds_bf16x8*)(X + kb * 32 * C::ROW_BYTES + (ch / C::NKOFF) * 256 +
+                                           k_off[ch % C::NKOFF]);
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf, f[ch], ch == 0 ? f32x16{} : s, 0, 0, 0);
+  }
+}
+
+// acc[db] += A^T * bf for the 16 contraction rows of chunk pc (A read
+// transposed from a V-swizzled tile).
+template <class C>
+__device__ __forceinline__ void tr_chunk(f32x16 (&acc)[C::DB], const lds_u8* tile,
+                                         const bf16x8& bf, const int (&v_off)[C::NVOFF], int pc) {
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) {
+    const lds_u8* p = tile + pc * 16 * C::ROW_BYTES + (db / C::NVOFF) * 256 + v_off[db % C::NVOFF];
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * C::ROW_BYTES));
+    const bf16x8 af =
+        __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc[db], 0, 0, 0);
+  }
+}
+
 // ----------------------------------------------------------------------------
 // dK, dV: one workgroup per (128 keys, head, batch)
 // ----------------------------------------------------------------------------
+// Query tiles t stream through LDS.  Step t computes, on the matrix cores,
+// S(t+1) and dP(t+1) for the next tile while the weights P(t) and dS(t) form,
+// then dV += P(t)^T dO(t) and dK += dS(t)^T q(t).  The row-layout copies of q
+// and dO (read by S and dP) therefore run one tile ahead of the transposed
+// copies (read by the dV and dK products) and of LSE and Delta.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void fa_bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -212,19 +252,24 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dkdv_kernel(
   const int my_k = kw0 + m;
 
   // Query tiles this workgroup visits: causal -- those with a query >= k0.
+  // A wave takes part in tile t when some query of the tile sees one of its
+  // keys (with the causal mask this holds for every tile after its first).
   const int nt = (S + 63) / 64;
   const int t_first = CAUSAL ? k0 / 64 : 0;
+  auto live = [&](int t) { return kw0 < S && (!CAUSAL || t * 64 + 63 >= kw0); };
 
   int qoff[C::LOADS_PER_WAVE], qrow[C::LOADS_PER_WAVE];
   int toff[C::LOADS_PER_WAVE], trow[C::LOADS_PER_WAVE];
   tile_offsets<C, false>(qoff, qrow, wave, lane);
   tile_offsets<C, true>(toff, trow, wave, lane);
-  auto copies = [&](int t, lds_u8* qr, lds_u8* qt, lds_u8* dr, lds_u8* dt, lds_u8* ls,
-                    lds_u8* de) {
+  auto copy_rows = [&](int t, lds_u8* qr, lds_u8* dr) {
     const int q0 = t * 64;
     issue_tile<C>(Qh, qr, q0, S, wave, qoff, qrow);
-    issue_tile<C>(Qh, qt, q0, S, wave, toff, trow);
     issue_tile<C>(dOh, dr, q0, S, wave, qoff, qrow);
+  };
+  auto copy_cols = [&](int t, lds_u8* qt, lds_u8* dt, lds_u8* ls, lds_u8* de) {
+    const int q0 = t * 64;
+    issue_tile<C>(Qh, qt, q0, S, wave, toff, trow);
     issue_tile<C>(dOh, dt, q0, S, wave, toff, trow);
     if (wave == 0) issue_rowvec(LSEh, ls, q0, S, lane);
     if (wave == 1) issue_rowvec(Dh, de, q0, S, lane);
@@ -242,64 +287,98 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dkdv_kernel(
     dk_acc[db] = f32x16{};
     dv_acc[db] = f32x16{};
   }
-  constexpr float kL2e = kLog2e;
 
-  if (t_first < nt) copies(t_first, qr0, qt0, dr0, dt0, ls0, de0);
+  if (t_first < nt) {
+    copy_rows(t_first, qr0, dr0);
+    copy_cols(t_first, qt0, dt0, ls0, de0);
+  }
+  if (t_first + 1 < nt) copy_rows(t_first + 1, qr1, dr1);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  // S and dP tiles in two named sets used alternately.
+  f32x16 s_a[C::KB], dp_a[C::KB], s_b[C::KB], dp_b[C::KB];
+  if (t_first < nt && live(t_first)) {
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb) {
+      qk_block<C>(s_a[kb], qr0, kf, k_off, kb);
+      qk_block<C>(dp_a[kb], dr0, vf, k_off, kb);
+    }
+  }
+  __syncthreads();  // every wave is done with the rows of the first tile
 
-  // Tile t (query rows q0 .. q0+63): start the copies of tile t+1, then
-  // S, dP, P, dS and the two products for this wave's 32 keys.
-  auto step = [&](const int t, const lds_u8* qr, const lds_u8* qt, const lds_u8* dr,
-                  const lds_u8* dt, const lds_u8* ls, const lds_u8* de, lds_u8* nqr,
-                  lds_u8* nqt, lds_u8* ndr, lds_u8* ndt, lds_u8* nls, lds_u8* nde) {
-    if (t + 1 < nt) copies(t + 1, nqr, nqt, ndr, ndt, nls, nde);
+  // Step t: start the row copies of tile t+2 and the transposed copies (and
+  // LSE, Delta) of tile t+1; S(t+1), dP(t+1) into s_out, dp_out while P(t),
+  // dS(t) form from s_in, dp_in; then the dV and dK products of tile t.
+  auto step = [&](const int t, const lds_u8* qr_n, const lds_u8* dr_n, lds_u8* qr_l,
+                  lds_u8* dr_l, const lds_u8* qt, const lds_u8* dt, const lds_u8* ls,
+                  const lds_u8* de, lds_u8* qt_l, lds_u8* dt_l, lds_u8* ls_l, lds_u8* de_l,
+                  f32x16 (&s_in)[C::KB], f32x16 (&dp_in)[C::KB], f32x16 (&s_out)[C::KB],
+                  f32x16 (&dp_out)[C::KB]) {
+    if (t + 2 < nt) copy_rows(t + 2, qr_l, dr_l);
+    if (t + 1 < nt) copy_cols(t + 1, qt_l, dt_l, ls_l, de_l);
     const int q0 = t * 64;
-    // causal: this wave's keys are seen only by queries >= kw0
-    if (kw0 < S && (!CAUSAL || q0 + 63 >= kw0)) {
-      f32x16 s[C::KB], dp[C::KB];
-      qk_tile<C>(s, qr, kf, k_off);    // S[q][key]  (rows: queries, lane: key)
-      qk_tile<C>(dp, dr, vf, k_off);   // dP[q][key]
-      const bool masked = (CAUSAL && q0 < kw0 + 31) || (q0 + 64 > S);
+    if (live(t)) {
+      // ---- mask (diagonal and tail tiles): excluded scores -> -inf ------------
+      if ((CAUSAL && q0 < kw0 + 31) || (q0 + 64 > S)) {
+#pragma unroll
+        for (int qb = 0; qb < C::KB; ++qb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            // register r of block qb holds query row 32*qb + 16*(r/8) + 8*hh + r%8
+            const int q = q0 + 32 * qb + 16 * (r >> 3) + 8 * hh + (r & 7);
+            if (q >= S || (CAUSAL && my_k > q)) s_in[qb][r] = -INFINITY;
+          }
+      }
       bf16x8 pq[C::PCH], dsq[C::PCH];
+      // weights and dS of the 16-query chunk pc (registers 8*half .. +7 of block qb)
+      auto chunk = [&](int qb, int half) {
+        const int rb = 32 * qb + 16 * half + 8 * hh;
+        const int pc = 2 * qb + half;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int r = 8 * half + e;
+          const float lse2 = reinterpret_cast<const lds_f32*>(ls)[rb + e] * kLog2e;
+          const float del = reinterpret_cast<const lds_f32*>(de)[rb + e];
+          const float p = fast_exp2(fmaf(s_in[qb][r], c, -lse2));
+          pq[pc][e] = (__bf16)p;
+          dsq[pc][e] = (__bf16)(p * (dp_in[qb][r] - del));
+        }
+      };
+      // The products of a 16-query chunk follow the chunk's weights, and
+      // S(t+1), dP(t+1) are split around them, so the matrix cores always
+      // have independent work while the weights form.  (Pinning this order
+      // with scheduling barriers made the kernel slower: with one wavefront
+      // per SIMD the compiler's own interleave hides more of the LDS latency.)
 #pragma unroll
       for (int qb = 0; qb < C::KB; ++qb) {
+        qk_block<C>(s_out[qb], qr_n, kf, k_off, qb);
+        qk_block<C>(dp_out[qb], dr_n, vf, k_off, qb);
+        chunk(qb, 0);
+        chunk(qb, 1);
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-          // register r = 8*half + e holds query row 32*qb + 16*half + 8*hh + e
-          const int rb = 32 * qb + 16 * half + 8 * hh;
-          float lse8[8], del8[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            lse8[e] = reinterpret_cast<const lds_f32*>(ls)[rb + e];
-            del8[e] = reinterpret_cast<const lds_f32*>(de)[rb + e];
-          }
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int r = 8 * half + e;
-            float p = fast_exp2(fmaf(s[qb][r], c, -lse8[e] * kL2e));
-            if (masked) {
-              const int q = q0 + rb + e;
-              if (q >= S || (CAUSAL && my_k > q)) p = 0.0f;
-            }
-            const float ds = p * (dp[qb][r] - del8[e]);
-            pq[2 * qb + half][e] = (__bf16)p;
-            dsq[2 * qb + half][e] = (__bf16)ds;
-          }
+          tr_chunk<C>(dv_acc, dt, pq[2 * qb + half], v_off, 2 * qb + half);   // dV^T += dO^T P
+          tr_chunk<C>(dk_acc, qt, dsq[2 * qb + half], v_off, 2 * qb + half);  // dK^T += q^T dS
         }
       }
-      tr_product<C>(dv_acc, dt, pq, v_off);   // dV^T += dO^T P
-      tr_product<C>(dk_acc, qt, dsq, v_off);  // dK^T += q^T dS
+    } else if (t + 1 < nt && live(t + 1)) {
+      // the wave's first tile is the next one: only S(t+1), dP(t+1)
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb) {
+        qk_block<C>(s_out[kb], qr_n, kf, k_off, kb);
+        qk_block<C>(dp_out[kb], dr_n, vf, k_off, kb);
+      }
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
   int t = t_first;
   for (; t + 1 < nt; t += 2) {
-    step(t, qr0, qt0, dr0, dt0, ls0, de0, qr1, qt1, dr1, dt1, ls1, de1);
-    step(t + 1, qr1, qt1, dr1, dt1, ls1, de1, qr0, qt0, dr0, dt0, ls0, de0);
+    step(t, qr1, dr1, qr0, dr0, qt0, dt0, ls0, de0, qt1, dt1, ls1, de1, s_a, dp_a, s_b, dp_b);
+    step(t + 1, qr0, dr0, qr1, dr1, qt1, dt1, ls1, de1, qt0, dt0, ls0, de0, s_b, dp_b, s_a, dp_a);
   }
-  if (t < nt) step(t, qr0, qt0, dr0, dt0, ls0, de0, qr1, qt1, dr1, dt1, ls1, de1);
+  if (t < nt)
+    step(t, qr1, dr1, qr0, dr0, qt0, dt0, ls0, de0, qt1, dt1, ls1, de1, s_a, dp_a, s_b, dp_b);
 
   if (my_k >= S) return;
   store_col<C::DB>(dK + head + (size_t)my_k * D, dk_acc, scale, hh);
@@ -307,15 +386,15 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dkdv_kernel(
 }
 
 // ----------------------------------------------------------------------------
-// dQ: one workgroup per (128 queries, head, batch)
+// dQ: one workgroup per (256 queries, head, batch)
 // ----------------------------------------------------------------------------
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void fa_bwd_dq_kernel(
+template <int D, int WAVES, bool CAUSAL>
+__global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 2 : 1) void fa_bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Delta, uint16_t* __restrict__ dQ,
     int S, int nq, int bh_total, int group_heads, float c, float scale) {
-  using C = BfCfg<D, 64, 4>;  // key tiles of 64; 4 waves of 32 queries
+  using C = BfCfg<D, 64, WAVES>;  // key tiles of 64; waves of 32 queries
   // K tile in two layouts (row reads for S^T, transposed reads for dq), V
   // tile row-wise (for dP^T); two stages.
   __shared__ __attribute__((aligned(1024))) uint8_t kr0_raw[C::TILE_BYTES];
@@ -345,24 +424,28 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dq_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m = lane & 31;
   const int hh = lane >> 5;
-  const int q0 = qt * 128;
+  const int q0 = qt * C::BR;
   const int qw0 = q0 + wave * kRowsPerWave;
   const int my_q = qw0 + m;
 
-  const int kend = CAUSAL ? min(S, q0 + 128) : S;
+  const int kend = CAUSAL ? min(S, q0 + C::BR) : S;
   const int ntiles = (kend + 63) / 64;
   const int wave_klast = CAUSAL ? min(qw0 + kRowsPerWave - 1, S - 1) : (S - 1);
   const int wave_ntiles = qw0 < S ? min(ntiles, wave_klast / 64 + 1) : 0;
 
-  int koff[C::LOADS_PER_WAVE], krow[C::LOADS_PER_WAVE];
-  int toff[C::LOADS_PER_WAVE], trow[C::LOADS_PER_WAVE];
-  tile_offsets<C, false>(koff, krow, wave, lane);
-  tile_offsets<C, true>(toff, trow, wave, lane);
+  const bool copier = wave < C::COPY_WAVES;
+  const int cw = copier ? wave : 0;  // this wave's share of each tile copy
+  // The copy offsets are recomputed at each copy (a few instructions, copier
+  // waves only) rather than held in registers through the loop.
   auto copies = [&](int j, lds_u8* kr, lds_u8* ktt, lds_u8* vr) {
+    if (!copier) return;
+    int off[C::LOADS_PER_WAVE], row[C::LOADS_PER_WAVE];
     const int k0 = j * 64;
-    issue_tile<C>(Kh, kr, k0, S, wave, koff, krow);
-    issue_tile<C>(Kh, ktt, k0, S, wave, toff, trow);
-    issue_tile<C>(Vh, vr, k0, S, wave, koff, krow);
+    tile_offsets<C, false>(off, row, cw, lane);
+    issue_tile<C>(Kh, kr, k0, S, cw, off, row);
+    issue_tile<C>(Vh, vr, k0, S, cw, off, row);
+    tile_offsets<C, true>(off, row, cw, lane);
+    issue_tile<C>(Kh, ktt, k0, S, cw, off, row);
   };
 
   bf16x8 qf[C::KCH], df[C::KCH];
@@ -454,11 +537,13 @@ int run_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint1
     st = launch_k(fa_bwd_dkdv_kernel<D, false>, grid, 256, s, q, k, v, dout, (const float*)lse,
                   (const float*)delta, dk, dv, S, nk, bh, group_heads, c, scale);
   if (st != FA_OK) return st;
+  const int nq = (S + 255) / 256;
+  const unsigned gq = (unsigned)nq * (unsigned)bh;
   if (causal)
-    return launch_k(fa_bwd_dq_kernel<D, true>, grid, 256, s, q, k, v, dout, (const float*)lse,
-                    (const float*)delta, dq, S, nk, bh, group_heads, c, scale);
-  return launch_k(fa_bwd_dq_kernel<D, false>, grid, 256, s, q, k, v, dout, (const float*)lse,
-                  (const float*)delta, dq, S, nk, bh, group_heads, c, scale);
+    return launch_k(fa_bwd_dq_kernel<D, 8, true>, gq, 512, s, q, k, v, dout, (const float*)lse,
+                    (const float*)delta, dq, S, nq, bh, group_heads, c, scale);
+  return launch_k(fa_bwd_dq_kernel<D, 8, false>, gq, 512, s, q, k, v, dout, (const float*)lse,
+                  (const float*)delta, dq, S, nq, bh, group_heads, c, scale);
 }
 
 }  // namespace

@@ -65,8 +65,10 @@ def check_grads(got, ref, label):
         assert mx <= MAX_REL, (label, name, mx)
 
 
+# S = 777: several 256-query dq blocks with a ragged tail, an odd number of
+# 128-key dk/dv blocks
 SHAPES = [(1, 2, 17), (2, 2, 64), (1, 3, 65), (1, 2, 127), (2, 1, 128), (1, 2, 129), (2, 2, 200),
-          (1, 2, 300), (1, 1, 511)]
+          (1, 2, 300), (1, 1, 511), (1, 2, 777)]
 CASES = [(B, H, S, D, c) for (B, H, S) in SHAPES for D in (64, 128) for c in (False, True)]
 
 
