@@ -31,7 +31,8 @@
 //    queries, head, batch), two wavefronts per SIMD as in the forward; waves
 //    0-3 issue the tile copies.  The forward's layout (one query per lane):
 //    S^T = K q^T, dP^T = V dO^T, dS^T, then dq^T += K^T dS^T with K read
-//    transposed.
+//    transposed.  K and V tiles are stored in one swizzle that serves both the
+//    row reads and the transposing reads, so each K tile is copied once.
 // No atomics and no workspace beyond the caller's Delta buffer: dq is
 // accumulated by the workgroup that owns the query tile.
 
@@ -385,6 +386,68 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dkdv_kernel(
   store_col<C::DB>(dV + head + (size_t)my_k * D, dv_acc, 1.0f, hh);
 }
 
+// One swizzle for tiles read both row-wise (16 rows of one chunk column per
+// pass) and with the transposing read (4 consecutive rows x 4 chunks per
+// pass), conflict-free for both: a bijection of the 16 rows of a pass onto
+// chunk slots that also sends 4 consecutive rows to distinct 64-byte groups.
+template <class C>
+__device__ __forceinline__ int uswz(int r) {
+  static_assert(C::ROW_BYTES == 256 || C::ROW_BYTES == 128, "unified swizzle: D = 64 or 128");
+  if constexpr (C::ROW_BYTES == 256) return ((r & 3) << 2) | ((r >> 2) & 3);
+  return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+// Copy offsets and operand-read offsets for the unified swizzle.
+template <class C>
+__device__ __forceinline__ void tile_offsets_u(int* off, int* row, int part, int lane) {
+#pragma unroll
+  for (int u = 0; u < C::LOADS_PER_WAVE; ++u) {
+    const int n = part * C::LOADS_PER_WAVE + u;
+    const int r = n * C::ROWS_PER_LOAD + lane / C::RC;
+    row[u] = r;
+    off[u] = r * C::D + ((lane % C::RC) ^ uswz<C>(r)) * 8;
+  }
+}
+// (v_off: the transposing read's first half, rows R; v_hi: second half, rows
+// R + 4, whose swizzle differs.)
+template <class C>
+__device__ __forceinline__ void operand_offsets_u(int lane, int (&k_off)[C::NKOFF],
+                                                  int (&v_off)[C::NVOFF], int (&v_hi)[C::NVOFF]) {
+  const int m = lane & 31, hh = lane >> 5;
+  const int pm = key_perm(m);
+  const int ksw = uswz<C>(pm);
+#pragma unroll
+  for (int b = 0; b < C::NKOFF; ++b) k_off[b] = pm * C::ROW_BYTES + (((2 * b + hh) ^ ksw) << 4);
+  const int g = lane >> 4, j4 = (lane >> 2) & 3, t4 = lane & 3;
+  const int vx = 2 * (g & 1) + (t4 >> 1);
+  const int vsw = uswz<C>(hh * 8 + j4), vsw4 = uswz<C>(hh * 8 + j4 + 4);
+  const int v_row = (hh * 8 + j4) * C::ROW_BYTES + (t4 & 1) * 8;
+#pragma unroll
+  for (int d4 = 0; d4 < C::NVOFF; ++d4) {
+    v_off[d4] = v_row + (((4 * d4 + vx) ^ vsw) << 4);
+    v_hi[d4] = v_row + 4 * C::ROW_BYTES + (((4 * d4 + vx) ^ vsw4) << 4);
+  }
+}
+
+// acc[db] += A^T * bf, A read transposed from a tile in the unified swizzle.
+template <class C>
+__device__ __forceinline__ void tr_product_u(f32x16 (&acc)[C::DB], const lds_u8* tile,
+                                             const bf16x8 (&bf)[C::PCH],
+                                             const int (&v_off)[C::NVOFF],
+                                             const int (&v_hi)[C::NVOFF]) {
+#pragma unroll
+  for (int pc = 0; pc < C::PCH; ++pc)
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      const lds_u8* b = tile + pc * 16 * C::ROW_BYTES + (db / C::NVOFF) * 256;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b + v_off[db % C::NVOFF]));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b + v_hi[db % C::NVOFF]));
+      const bf16x8 af =
+          __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf[pc], acc[db], 0, 0, 0);
+    }
+}
+
 // ----------------------------------------------------------------------------
 // dQ: one workgroup per (256 queries, head, batch)
 // ----------------------------------------------------------------------------
@@ -399,14 +462,10 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 2 : 1) void fa_bwd_dq_kern
   // tile row-wise (for dP^T); two stages.
   __shared__ __attribute__((aligned(1024))) uint8_t kr0_raw[C::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t kr1_raw[C::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t kt0_raw[C::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t kt1_raw[C::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t vr0_raw[C::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t vr1_raw[C::TILE_BYTES];
   lds_u8* kr0 = (lds_u8*)kr0_raw;
   lds_u8* kr1 = (lds_u8*)kr1_raw;
-  lds_u8* kt0 = (lds_u8*)kt0_raw;
-  lds_u8* kt1 = (lds_u8*)kt1_raw;
   lds_u8* vr0 = (lds_u8*)vr0_raw;
   lds_u8* vr1 = (lds_u8*)vr1_raw;
 
@@ -437,22 +496,20 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 2 : 1) void fa_bwd_dq_kern
   const int cw = copier ? wave : 0;  // this wave's share of each tile copy
   // The copy offsets are recomputed at each copy (a few instructions, copier
   // waves only) rather than held in registers through the loop.
-  auto copies = [&](int j, lds_u8* kr, lds_u8* ktt, lds_u8* vr) {
+  auto copies = [&](int j, lds_u8* kr, lds_u8* vr) {
     if (!copier) return;
     int off[C::LOADS_PER_WAVE], row[C::LOADS_PER_WAVE];
     const int k0 = j * 64;
-    tile_offsets<C, false>(off, row, cw, lane);
+    tile_offsets_u<C>(off, row, cw, lane);
     issue_tile<C>(Kh, kr, k0, S, cw, off, row);
     issue_tile<C>(Vh, vr, k0, S, cw, off, row);
-    tile_offsets<C, true>(off, row, cw, lane);
-    issue_tile<C>(Kh, ktt, k0, S, cw, off, row);
   };
 
   bf16x8 qf[C::KCH], df[C::KCH];
   row_fragments<C>(qf, Qh, my_q, S, hh);
   row_fragments<C>(df, dOh, my_q, S, hh);
-  int k_off[C::NKOFF], v_off[C::NVOFF];
-  operand_offsets<C>(lane, k_off, v_off);
+  int k_off[C::NKOFF], v_off[C::NVOFF], v_hi[C::NVOFF];
+  operand_offsets_u<C>(lane, k_off, v_off, v_hi);
   const float lse2 = my_q < S ? LSE[(size_t)bh * S + my_q] * kLog2e : 0.0f;
   const float delta = my_q < S ? Delta[(size_t)bh * S + my_q] : 0.0f;
 
@@ -460,13 +517,12 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 2 : 1) void fa_bwd_dq_kern
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
 
-  if (ntiles > 0) copies(0, kr0, kt0, vr0);
+  if (ntiles > 0) copies(0, kr0, vr0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  auto step = [&](const int j, const lds_u8* kr, const lds_u8* ktt, const lds_u8* vr,
-                  lds_u8* nkr, lds_u8* nkt, lds_u8* nvr) {
-    if (j + 1 < ntiles) copies(j + 1, nkr, nkt, nvr);
+  auto step = [&](const int j, const lds_u8* kr, const lds_u8* vr, lds_u8* nkr, lds_u8* nvr) {
+    if (j + 1 < ntiles) copies(j + 1, nkr, nvr);
     if (j < wave_ntiles) {
       const int k0 = j * 64;
       f32x16 s[C::KB], dp[C::KB];
@@ -484,17 +540,17 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 2 : 1) void fa_bwd_dq_kern
           if (masked && kb * 32 + (r >> 3) * 16 + (r & 7) > lim) p = 0.0f;
           dsf[2 * kb + (r >> 3)][r & 7] = (__bf16)(p * (dp[kb][r] - delta));
         }
-      tr_product<C>(acc, ktt, dsf, v_off);  // dq^T += K^T dS^T
+      tr_product_u<C>(acc, kr, dsf, v_off, v_hi);  // dq^T += K^T dS^T
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
   int j = 0;
   for (; j + 1 < ntiles; j += 2) {
-    step(j, kr0, kt0, vr0, kr1, kt1, vr1);
-    step(j + 1, kr1, kt1, vr1, kr0, kt0, vr0);
+    step(j, kr0, vr0, kr1, vr1);
+    step(j + 1, kr1, vr1, kr0, vr0);
   }
-  if (j < ntiles) step(j, kr0, kt0, vr0, kr1, kt1, vr1);
+  if (j < ntiles) step(j, kr0, vr0, kr1, vr1);
 
   if (my_q >= S) return;
   store_col<C::DB>(dQ + head + (size_t)my_q * D, acc, scale, hh);
