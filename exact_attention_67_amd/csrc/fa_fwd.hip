@@ -849,18 +849,22 @@ struct LaunchCfg {
 // registers).  Workgroup size: an 8-wave workgroup (256 query rows) shares
 // each staged K/V tile among twice as many rows as a 4-wave one, halving the
 // global->LDS copy volume per flop.  At D = 128 that pays when the grid still
-// holds enough workgroups to balance: one per CU without a mask, two per CU
-// with the causal mask, whose workgroups differ in length.  At D = 64 the
-// exponentials, not the copies, dominate, and D = 256 runs one wave per SIMD.
-LaunchCfg bf16_config(int S, int D, bool causal, int bh_total) {  // S: query rows
+// holds enough workgroups to balance: one per CU when the workgroups are of
+// about equal length (no mask, or queries behind a key prefix at least as
+// long as themselves, so the longest query tile's keys exceed the mean by at
+// most a third), two per CU otherwise (the causal mask over a square
+// sequence: lengths 1..n).  At D = 64 the exponentials, not the copies,
+// dominate, and D = 256 runs one wave per SIMD.
+LaunchCfg bf16_config(int Sq, int Sk, int D, bool causal, int bh_total) {
   constexpr int64_t kCUs = 256;
   LaunchCfg cfg;
   cfg.bc = D == 256 ? 32 : 64;
   cfg.waves = 4;
-  if (D == 128 && (int64_t)((S + 255) / 256) * bh_total >= (causal ? 2 : 1) * kCUs)
+  const bool even = !causal || (int64_t)Sk - Sq >= Sq;
+  if (D == 128 && (int64_t)((Sq + 255) / 256) * bh_total >= (even ? 1 : 2) * kCUs)
     cfg.waves = 8;
   const int br = kRowsPerWave * cfg.waves;
-  cfg.nq = (S + br - 1) / br;
+  cfg.nq = (Sq + br - 1) / br;
   cfg.grid = (unsigned)cfg.nq * (unsigned)bh_total;
   return cfg;
 }
@@ -906,7 +910,7 @@ int fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, i
   const int st = validate(q, k, v, o, lse, B, H, Sq, Sk, D, causal, scale, 2, &p);
   if (st != FA_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const LaunchCfg cfg = bf16_config(Sq, D, causal, p.bh_total);
+  const LaunchCfg cfg = bf16_config(Sq, Sk, D, causal, p.bh_total);
   switch (D) {
     case 64: return run_bf16<64, 64, 4>(q, k, v, o, lse, Sq, Sk, causal, p, cfg, s);
     case 128:
@@ -1081,7 +1085,7 @@ extern "C" int fa_fwd_plan(int B, int H, int S, int D, int causal, int elem_byte
   const int bh = B * H;
   int rows, keys, thr, grid;
   if (elem_bytes == 2) {
-    const LaunchCfg cfg = bf16_config(S, D, causal != 0, bh);
+    const LaunchCfg cfg = bf16_config(S, S, D, causal != 0, bh);
     rows = kRowsPerWave * cfg.waves;
     keys = cfg.bc;
     thr = 64 * cfg.waves;
