@@ -181,7 +181,8 @@ def time_secondary(steps):
         log(f"[bench] {name}: {avg:.4f} ms, {out[name]['tflops']} TFLOP/s, "
             f"K/V read {out[name]['kv_read_gbs']} GB/s")
         del q, k, v, o, lse
-    for name in ("c3_bf16_2x16x4096x128", "c4_bf16_causal_1x32x16384x128"):
+    for name in ("c3_bf16_2x16x4096x128", "c4_bf16_causal_1x32x16384x128",
+                 "c5_bf16_causal_2x8x8192x256_stress"):
         w = wl.WORKLOADS[name]
         q, k, v = (t.cuda() for t in wl.make_inputs(w))
         g = torch.Generator("cpu").manual_seed(w.seed + 100)

@@ -26,10 +26,12 @@
 //    copied into LDS twice, once per swizzle.  Its registers (about 480 per
 //    lane) allow one wavefront per SIMD, so each wave overlaps its own work:
 //    S and dP of the next query tile are computed while the weights and dS
-//    of the current one form.
+//    of the current one form.  At D = 256 the query tiles are 32 rows and
+//    the head dimensions of dK and dV are split between two workgroups per
+//    key block (both compute S and dP), so that a part's accumulators fit.
 //  * fa_bwd_dq_kernel: one workgroup of 8 wavefronts per (block of 256
 //    queries, head, batch), two wavefronts per SIMD as in the forward; waves
-//    0-3 issue the tile copies.  The forward's layout (one query per lane):
+//    0-3 issue the tile copies.  (D = 256: 4 wavefronts, 32-key tiles.)  The forward's layout (one query per lane):
 //    S^T = K q^T, dP^T = V dO^T, dS^T, then dq^T += K^T dS^T with K read
 //    transposed.  K and V tiles are stored in one swizzle that serves both the
 //    row reads and the transposing reads, so each K tile is copied once.
@@ -170,14 +172,18 @@ __device__ __forceinline__ void qk_block(f32x16& s, const lds_u8* X, const bf16x
   }
 }
 
-// acc[db] += A^T * bf for the 16 contraction rows of chunk pc (A read
-// transposed from a V-swizzled tile).
-template <class C>
-__device__ __forceinline__ void tr_chunk(f32x16 (&acc)[C::DB], const lds_u8* tile,
-                                         const bf16x8& bf, const int (&v_off)[C::NVOFF], int pc) {
+// acc[hb] += A^T * bf for the 16 contraction rows of chunk pc (A read
+// transposed from a V-swizzled tile), for NB 32-wide head-dim blocks starting
+// at block part * NB.
+template <class C, int NB>
+__device__ __forceinline__ void tr_chunk(f32x16 (&acc)[NB], const lds_u8* tile,
+                                         const bf16x8& bf, const int (&v_off)[C::NVOFF], int pc,
+                                         int part) {
+  static_assert(NB % C::NVOFF == 0, "a head-dim part spans whole offset groups");
+  const lds_u8* t = tile + pc * 16 * C::ROW_BYTES + part * (NB / C::NVOFF) * 256;
 #pragma unroll
-  for (int db = 0; db < C::DB; ++db) {
-    const lds_u8* p = tile + pc * 16 * C::ROW_BYTES + (db / C::NVOFF) * 256 + v_off[db % C::NVOFF];
+  for (int db = 0; db < NB; ++db) {
+    const lds_u8* p = t + (db / C::NVOFF) * 256 + v_off[db % C::NVOFF];
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * C::ROW_BYTES));
     const bf16x8 af =
@@ -194,14 +200,18 @@ __device__ __forceinline__ void tr_chunk(f32x16 (&acc)[C::DB], const lds_u8* til
 // then dV += P(t)^T dO(t) and dK += dS(t)^T q(t).  The row-layout copies of q
 // and dO (read by S and dP) therefore run one tile ahead of the transposed
 // copies (read by the dV and dK products) and of LSE and Delta.
-template <int D, bool CAUSAL>
+template <int D, int BQ, int NP, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void fa_bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Delta, uint16_t* __restrict__ dK,
     uint16_t* __restrict__ dV, int S, int nk, int bh_total, int group_heads, float c,
     float scale) {
-  using C = BfCfg<D, 64, 4>;  // query tiles of 64 rows; 4 waves of 32 keys
+  using C = BfCfg<D, BQ, 4>;  // query tiles of BQ rows; 4 waves of 32 keys
+  // The head dimensions of dK and dV are split into NP parts, one workgroup
+  // each (NP = 2 at D = 256, where two full accumulators do not fit beside
+  // the K and V fragments); every part computes the full S and dP.
+  constexpr int NB = C::DB / NP;  // 32-wide head-dim blocks of this part
   // Query tile in two layouts (row reads: K swizzle; transposed reads: V
   // swizzle) for q and dO, two stages; each a separately named array.
   __shared__ __attribute__((aligned(1024))) uint8_t qr0_raw[C::TILE_BYTES];
@@ -231,8 +241,9 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dkdv_kernel(
 
   // Heaviest key blocks (the first ones, seen by most query tiles) first.
   int bh, kt;
-  decode_tile<CAUSAL>(xcd_logical_index(blockIdx.x, nk * bh_total), nk, bh_total, group_heads,
-                      bh, kt);
+  const int L = xcd_logical_index(blockIdx.x, nk * bh_total * NP);  // parts adjacent: same XCD
+  const int part = L % NP;
+  decode_tile<CAUSAL>(L / NP, nk, bh_total, group_heads, bh, kt);
   if (CAUSAL) kt = nk - 1 - kt;
 
   const size_t head = (size_t)bh * (size_t)S * D;
@@ -255,21 +266,21 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dkdv_kernel(
   // Query tiles this workgroup visits: causal -- those with a query >= k0.
   // A wave takes part in tile t when some query of the tile sees one of its
   // keys (with the causal mask this holds for every tile after its first).
-  const int nt = (S + 63) / 64;
-  const int t_first = CAUSAL ? k0 / 64 : 0;
-  auto live = [&](int t) { return kw0 < S && (!CAUSAL || t * 64 + 63 >= kw0); };
+  const int nt = (S + BQ - 1) / BQ;
+  const int t_first = CAUSAL ? k0 / BQ : 0;
+  auto live = [&](int t) { return kw0 < S && (!CAUSAL || t * BQ + BQ - 1 >= kw0); };
 
   int qoff[C::LOADS_PER_WAVE], qrow[C::LOADS_PER_WAVE];
   int toff[C::LOADS_PER_WAVE], trow[C::LOADS_PER_WAVE];
   tile_offsets<C, false>(qoff, qrow, wave, lane);
   tile_offsets<C, true>(toff, trow, wave, lane);
   auto copy_rows = [&](int t, lds_u8* qr, lds_u8* dr) {
-    const int q0 = t * 64;
+    const int q0 = t * BQ;
     issue_tile<C>(Qh, qr, q0, S, wave, qoff, qrow);
     issue_tile<C>(dOh, dr, q0, S, wave, qoff, qrow);
   };
   auto copy_cols = [&](int t, lds_u8* qt, lds_u8* dt, lds_u8* ls, lds_u8* de) {
-    const int q0 = t * 64;
+    const int q0 = t * BQ;
     issue_tile<C>(Qh, qt, q0, S, wave, toff, trow);
     issue_tile<C>(dOh, dt, q0, S, wave, toff, trow);
     if (wave == 0) issue_rowvec(LSEh, ls, q0, S, lane);
@@ -282,9 +293,9 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dkdv_kernel(
   int k_off[C::NKOFF], v_off[C::NVOFF];
   operand_offsets<C>(lane, k_off, v_off);
 
-  f32x16 dk_acc[C::DB], dv_acc[C::DB];
+  f32x16 dk_acc[NB], dv_acc[NB];
 #pragma unroll
-  for (int db = 0; db < C::DB; ++db) {
+  for (int db = 0; db < NB; ++db) {
     dk_acc[db] = f32x16{};
     dv_acc[db] = f32x16{};
   }
@@ -317,10 +328,10 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dkdv_kernel(
                   f32x16 (&dp_out)[C::KB]) {
     if (t + 2 < nt) copy_rows(t + 2, qr_l, dr_l);
     if (t + 1 < nt) copy_cols(t + 1, qt_l, dt_l, ls_l, de_l);
-    const int q0 = t * 64;
+    const int q0 = t * BQ;
     if (live(t)) {
       // ---- mask (diagonal and tail tiles): excluded scores -> -inf ------------
-      if ((CAUSAL && q0 < kw0 + 31) || (q0 + 64 > S)) {
+      if ((CAUSAL && q0 < kw0 + 31) || (q0 + BQ > S)) {
 #pragma unroll
         for (int qb = 0; qb < C::KB; ++qb)
 #pragma unroll
@@ -358,8 +369,8 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dkdv_kernel(
         chunk(qb, 1);
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-          tr_chunk<C>(dv_acc, dt, pq[2 * qb + half], v_off, 2 * qb + half);   // dV^T += dO^T P
-          tr_chunk<C>(dk_acc, qt, dsq[2 * qb + half], v_off, 2 * qb + half);  // dK^T += q^T dS
+          tr_chunk<C, NB>(dv_acc, dt, pq[2 * qb + half], v_off, 2 * qb + half, part);   // dV^T += dO^T P
+          tr_chunk<C, NB>(dk_acc, qt, dsq[2 * qb + half], v_off, 2 * qb + half, part);  // dK^T += q^T dS
         }
       }
     } else if (t + 1 < nt && live(t + 1)) {
@@ -382,8 +393,8 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dkdv_kernel(
     step(t, qr1, dr1, qr0, dr0, qt0, dt0, ls0, de0, qt1, dt1, ls1, de1, s_a, dp_a, s_b, dp_b);
 
   if (my_k >= S) return;
-  store_col<C::DB>(dK + head + (size_t)my_k * D, dk_acc, scale, hh);
-  store_col<C::DB>(dV + head + (size_t)my_k * D, dv_acc, 1.0f, hh);
+  store_col<NB>(dK + head + (size_t)my_k * D + part * NB * 32, dk_acc, scale, hh);
+  store_col<NB>(dV + head + (size_t)my_k * D + part * NB * 32, dv_acc, 1.0f, hh);
 }
 
 // One swizzle for tiles read both row-wise (16 rows of one chunk column per
@@ -392,8 +403,10 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dkdv_kernel(
 // chunk slots that also sends 4 consecutive rows to distinct 64-byte groups.
 template <class C>
 __device__ __forceinline__ int uswz(int r) {
-  static_assert(C::ROW_BYTES == 256 || C::ROW_BYTES == 128, "unified swizzle: D = 64 or 128");
-  if constexpr (C::ROW_BYTES == 256) return ((r & 3) << 2) | ((r >> 2) & 3);
+  static_assert(C::ROW_BYTES == 512 || C::ROW_BYTES == 256 || C::ROW_BYTES == 128,
+                "unified swizzle: D = 64, 128 or 256");
+  // (512-byte rows: two bank lines per row; the XOR stays within a line)
+  if constexpr (C::ROW_BYTES >= 256) return ((r & 3) << 2) | ((r >> 2) & 3);
   return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
@@ -451,13 +464,13 @@ __device__ __forceinline__ void tr_product_u(f32x16 (&acc)[C::DB], const lds_u8*
 // ----------------------------------------------------------------------------
 // dQ: one workgroup per (256 queries, head, batch)
 // ----------------------------------------------------------------------------
-template <int D, int WAVES, bool CAUSAL>
+template <int D, int BC, int WAVES, bool CAUSAL>
 __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 2 : 1) void fa_bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Delta, uint16_t* __restrict__ dQ,
     int S, int nq, int bh_total, int group_heads, float c, float scale) {
-  using C = BfCfg<D, 64, WAVES>;  // key tiles of 64; waves of 32 queries
+  using C = BfCfg<D, BC, WAVES>;  // key tiles of BC; waves of 32 queries
   // K tile in two layouts (row reads for S^T, transposed reads for dq), V
   // tile row-wise (for dP^T); two stages.
   __shared__ __attribute__((aligned(1024))) uint8_t kr0_raw[C::TILE_BYTES];
@@ -488,9 +501,9 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 2 : 1) void fa_bwd_dq_kern
   const int my_q = qw0 + m;
 
   const int kend = CAUSAL ? min(S, q0 + C::BR) : S;
-  const int ntiles = (kend + 63) / 64;
+  const int ntiles = (kend + BC - 1) / BC;
   const int wave_klast = CAUSAL ? min(qw0 + kRowsPerWave - 1, S - 1) : (S - 1);
-  const int wave_ntiles = qw0 < S ? min(ntiles, wave_klast / 64 + 1) : 0;
+  const int wave_ntiles = qw0 < S ? min(ntiles, wave_klast / BC + 1) : 0;
 
   const bool copier = wave < C::COPY_WAVES;
   const int cw = copier ? wave : 0;  // this wave's share of each tile copy
@@ -499,7 +512,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 2 : 1) void fa_bwd_dq_kern
   auto copies = [&](int j, lds_u8* kr, lds_u8* vr) {
     if (!copier) return;
     int off[C::LOADS_PER_WAVE], row[C::LOADS_PER_WAVE];
-    const int k0 = j * 64;
+    const int k0 = j * BC;
     tile_offsets_u<C>(off, row, cw, lane);
     issue_tile<C>(Kh, kr, k0, S, cw, off, row);
     issue_tile<C>(Vh, vr, k0, S, cw, off, row);
@@ -524,11 +537,11 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 2 : 1) void fa_bwd_dq_kern
   auto step = [&](const int j, const lds_u8* kr, const lds_u8* vr, lds_u8* nkr, lds_u8* nvr) {
     if (j + 1 < ntiles) copies(j + 1, nkr, nvr);
     if (j < wave_ntiles) {
-      const int k0 = j * 64;
+      const int k0 = j * BC;
       f32x16 s[C::KB], dp[C::KB];
       qk_tile<C>(s, kr, qf, k_off);   // S^T[key][q]
       qk_tile<C>(dp, vr, df, k_off);  // dP^T[key][q]
-      const bool masked = (CAUSAL && (k0 + 63 > qw0)) || (k0 + 64 > S);
+      const bool masked = (CAUSAL && (k0 + BC - 1 > qw0)) || (k0 + BC > S);
       const int lim = (CAUSAL ? min(my_q, S - 1) : (S - 1)) - k0 - hh * 8;
       bf16x8 dsf[C::PCH];
 #pragma unroll
@@ -584,22 +597,27 @@ int run_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint1
   int st = launch_k(fa_bwd_delta_kernel<D>, (unsigned)((rows * (D / 8) + 255) / 256), 256, s,
                     o, dout, delta, rows);
   if (st != FA_OK) return st;
+  // D = 256: 32-row query tiles (dK/dV) and 32-key tiles in 4-wave dQ
+  // workgroups (LDS and registers); otherwise 64 and 8 waves.
+  constexpr int BT = D == 256 ? 32 : 64;
+  constexpr int QW = D == 256 ? 4 : 8;
+  constexpr int NP = D == 256 ? 2 : 1;  // head-dim parts of dK/dV
   const int nk = (S + 127) / 128;
-  const unsigned grid = (unsigned)nk * (unsigned)bh;
+  const unsigned grid = (unsigned)nk * (unsigned)bh * NP;
   if (causal)
-    st = launch_k(fa_bwd_dkdv_kernel<D, true>, grid, 256, s, q, k, v, dout, (const float*)lse,
-                  (const float*)delta, dk, dv, S, nk, bh, group_heads, c, scale);
+    st = launch_k(fa_bwd_dkdv_kernel<D, BT, NP, true>, grid, 256, s, q, k, v, dout,
+                  (const float*)lse, (const float*)delta, dk, dv, S, nk, bh, group_heads, c, scale);
   else
-    st = launch_k(fa_bwd_dkdv_kernel<D, false>, grid, 256, s, q, k, v, dout, (const float*)lse,
-                  (const float*)delta, dk, dv, S, nk, bh, group_heads, c, scale);
+    st = launch_k(fa_bwd_dkdv_kernel<D, BT, NP, false>, grid, 256, s, q, k, v, dout,
+                  (const float*)lse, (const float*)delta, dk, dv, S, nk, bh, group_heads, c, scale);
   if (st != FA_OK) return st;
-  const int nq = (S + 255) / 256;
+  const int nq = (S + 32 * QW - 1) / (32 * QW);
   const unsigned gq = (unsigned)nq * (unsigned)bh;
   if (causal)
-    return launch_k(fa_bwd_dq_kernel<D, 8, true>, gq, 512, s, q, k, v, dout, (const float*)lse,
-                    (const float*)delta, dq, S, nq, bh, group_heads, c, scale);
-  return launch_k(fa_bwd_dq_kernel<D, 8, false>, gq, 512, s, q, k, v, dout, (const float*)lse,
-                  (const float*)delta, dq, S, nq, bh, group_heads, c, scale);
+    return launch_k(fa_bwd_dq_kernel<D, BT, QW, true>, gq, 64 * QW, s, q, k, v, dout,
+                    (const float*)lse, (const float*)delta, dq, S, nq, bh, group_heads, c, scale);
+  return launch_k(fa_bwd_dq_kernel<D, BT, QW, false>, gq, 64 * QW, s, q, k, v, dout,
+                  (const float*)lse, (const float*)delta, dq, S, nq, bh, group_heads, c, scale);
 }
 
 }  // namespace
@@ -610,12 +628,12 @@ extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o
                       void* stream) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !delta) return FA_ERR_NULL;
   if (B < 1 || H < 1 || S < 1) return FA_ERR_SHAPE;
-  if (D != 64 && D != 128) return FA_ERR_HEADDIM;
+  if (D != 64 && D != 128 && D != 256) return FA_ERR_HEADDIM;
   if (causal != 0 && causal != 1) return FA_ERR_CAUSAL;
   if (!(scale > 0.0f) || !isfinite(scale)) return FA_ERR_SCALE;
   const int64_t bh = (int64_t)B * H;
   const int64_t nk = ((int64_t)S + 127) / 128;
-  if (bh > INT32_MAX || (int64_t)S * D > INT32_MAX || nk * bh > INT32_MAX ||
+  if (bh > INT32_MAX || (int64_t)S * D > INT32_MAX || 2 * nk * bh > INT32_MAX ||
       (uint64_t)(bh * S * D) > (uint64_t)(SIZE_MAX / 4))
     return FA_ERR_SHAPE;
   const uintptr_t a16 = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o |
@@ -643,5 +661,7 @@ extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o
   auto* dV = static_cast<uint16_t*>(dv);
   if (D == 64)
     return run_bwd<64>(Q, Kp, Vp, O, dO, lse, dQ, dK, dV, delta, (int)bh, S, causal != 0, scale, s);
-  return run_bwd<128>(Q, Kp, Vp, O, dO, lse, dQ, dK, dV, delta, (int)bh, S, causal != 0, scale, s);
+  if (D == 128)
+    return run_bwd<128>(Q, Kp, Vp, O, dO, lse, dQ, dK, dV, delta, (int)bh, S, causal != 0, scale, s);
+  return run_bwd<256>(Q, Kp, Vp, O, dO, lse, dQ, dK, dV, delta, (int)bh, S, causal != 0, scale, s);
 }

@@ -141,7 +141,7 @@ int fa_merge(const void* o_parts, const float* lse_parts, int G, int B, int H, i
  *   delta   : float32 [B,H,S] buffer owned by the caller, overwritten with
  *             rowsum(dout * o) (an intermediate the kernels share; it is an
  *             output so that the call itself allocates nothing).
- *   D       : 64 or 128.
+ *   D       : 64, 128 or 256.
  *   B, H, S, causal, scale, stream : as for fa_fwd (same values as the
  *             forward call).
  * Computes, with P = exp(scale * q k^T - lse) (masked entries 0):
@@ -152,7 +152,7 @@ int fa_merge(const void* o_parts, const float* lse_parts, int G, int B, int H, i
  * accumulation; P and dS are rounded to bf16 (nearest even) before the
  * products they feed.  Alignment: pointers to bf16 tensors 16-byte aligned,
  * lse and delta 4-byte aligned.  dq, dk, dv and delta must not overlap each
- * other or any input.  Errors: as for fa_fwd (FA_ERR_HEADDIM for D = 256).
+ * other or any input.  Errors: as for fa_fwd.
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
            const float* lse, void* dq, void* dk, void* dv, float* delta,

@@ -150,7 +150,7 @@ def test_bwd_validation_errors():
         assert call_bwd(**{name: 0}) == fa.FA_ERR_NULL, name
     for bad in ({"B": 0}, {"S": 0}, {"H": -2}):
         assert call_bwd(**bad) == fa.FA_ERR_SHAPE, bad
-    for d in (32, 96, 256):
+    for d in (32, 96, 512):
         assert call_bwd(D=d) == fa.FA_ERR_HEADDIM, d
     assert call_bwd(causal=5) == fa.FA_ERR_CAUSAL
     assert call_bwd(scale=0.0) == fa.FA_ERR_SCALE

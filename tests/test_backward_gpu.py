@@ -69,7 +69,7 @@ def check_grads(got, ref, label):
 # 128-key dk/dv blocks
 SHAPES = [(1, 2, 17), (2, 2, 64), (1, 3, 65), (1, 2, 127), (2, 1, 128), (1, 2, 129), (2, 2, 200),
           (1, 2, 300), (1, 1, 511), (1, 2, 777)]
-CASES = [(B, H, S, D, c) for (B, H, S) in SHAPES for D in (64, 128) for c in (False, True)]
+CASES = [(B, H, S, D, c) for (B, H, S) in SHAPES for D in (64, 128, 256) for c in (False, True)]
 
 
 @pytest.mark.parametrize("B,H,S,D,causal", CASES,
@@ -83,7 +83,7 @@ def test_backward_parity(B, H, S, D, causal):
     check_grads((dq, dk, dv), ref, f"bwd B={B} H={H} S={S} D={D} causal={causal}")
 
 
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 128, 256])
 def test_backward_larger(D):
     B, H, S = 2, 4, 1024
     q, k, v = wl.make_qkv(B, H, S, D, torch.bfloat16, seed=13000 + D)
