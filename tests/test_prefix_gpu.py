@@ -116,6 +116,20 @@ def test_fwd_kv_256_row_workgroups(Sq, Sk):
     check(o, lse, o_ref, l_ref, f"kv 256-row groups Sq={Sq} Sk={Sk}")
 
 
+def test_fwd_kv_prefix_single_round_of_256_row_workgroups():
+    # queries behind a key prefix at least as long as themselves have nearly
+    # equal tiles: 256-row workgroups already at one per CU (300 of them here)
+    B, H, Sq, Sk, D = 1, 300, 200, 500, 128
+    q, k, v = _qkv(B, H, Sq, Sk, D, seed=6500)
+    s = _scale(D)
+    o, lse = fa.forward_kv(q.cuda(), k.cuda(), v.cuda(), causal=True, scale=s)
+    torch.cuda.synchronize()
+    for h in (0, 137, 299):
+        sl = (slice(0, 1), slice(h, h + 1))
+        o_ref, l_ref = pre.attention_prefix(q[sl], k[sl], v[sl], True, s)
+        check(o[sl], lse[sl], o_ref, l_ref, f"kv prefix one round h={h}")
+
+
 # ---------------------------------------------------------------------------
 # Compositions through fa_merge
 # ---------------------------------------------------------------------------
