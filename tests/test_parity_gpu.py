@@ -158,6 +158,24 @@ def test_workgroup_shapes(B, H, S, causal, rows):
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("causal", [False, True])
+def test_long_sequence_sampled_rows(D, causal):
+    # 131072 keys: 64-bit row offsets, and the running softmax carried over
+    # more than 2000 key tiles; rows checked one by one against the oracle
+    B, H, S = 1, 2, 131072
+    q, k, v = wl.make_qkv(B, H, S, D, torch.bfloat16, seed=17000 + D + causal)
+    scale = float(torch.tensor(1 / math.sqrt(D), dtype=torch.float32))
+    o, lse = run(q, k, v, causal, scale)
+    g = torch.Generator().manual_seed(18000 + D)
+    rows = sorted(set([0, 1, 63, 64, 255, 256, S // 2, S - 257, S - 2, S - 1] +
+                      torch.randint(0, S, (14,), generator=g).tolist()))
+    for h in range(H):
+        o_ref, l_ref = orc.attention_rows(q, k, v, causal, scale, 0, h, rows)
+        check(o[0, h, rows].unsqueeze(0), lse[0, h, rows].unsqueeze(0), o_ref.unsqueeze(0),
+              l_ref.unsqueeze(0), torch.bfloat16, f"long S={S} D={D} causal={causal} h={h}")
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
 def test_zero_keys_give_prefix_means(D):
     S = 200
     q, _, v = wl.make_qkv(1, 1, S, D, torch.bfloat16, seed=5)
