@@ -108,26 +108,6 @@ __device__ __forceinline__ void store_col(uint16_t* __restrict__ out_row, const 
     }
 }
 
-// acc[db] += A^T * Bfrag, A read transposed from a V-swizzled tile (rows =
-// the contraction index, 16 per step), the forward's P*V pattern.
-template <class C>
-__device__ __forceinline__ void tr_product(f32x16 (&acc)[C::DB], const lds_u8* tile,
-                                           const bf16x8 (&bf)[C::PCH],
-                                           const int (&v_off)[C::NVOFF]) {
-#pragma unroll
-  for (int pc = 0; pc < C::PCH; ++pc)
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db) {
-      const lds_u8* p = tile + pc * 16 * C::ROW_BYTES + (db / C::NVOFF) * 256 +
-                        v_off[db % C::NVOFF];
-      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
-      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * C::ROW_BYTES));
-      const bf16x8 af =
-          __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf[pc], acc[db], 0, 0, 0);
-    }
-}
-
 // Per-lane byte offsets for the row reads (A operand of qk_tile, rows read in
 // the permuted order) and the transposing reads of a tile; as in the forward.
 template <class C>
@@ -193,7 +173,7 @@ __device__ __forceinline__ void tr_chunk(f32x16 (&acc)[NB], const lds_u8* tile,
 }
 
 // ----------------------------------------------------------------------------
-// dK, dV: one workgroup per (128 keys, head, batch)
+// dK, dV: one workgroup per (128 keys, head, batch, head-dim part)
 // ----------------------------------------------------------------------------
 // Query tiles t stream through LDS.  Step t computes, on the matrix cores,
 // S(t+1) and dP(t+1) for the next tile while the weights P(t) and dS(t) form,
