@@ -1,12 +1,14 @@
-"""Fused exact attention forward for MI355X (gfx950).
+"""Fused exact attention for MI355X (gfx950).
 
 ``forward(q, k, v, causal, scale)`` takes torch tensors of shape
 [B, H, S, D] on the GPU (bf16 or float32, contiguous), allocates O and LSE with
 torch, and calls the C ABI (``fa_fwd`` / ``fa_fwd_f32``) on torch's current
-stream.  ``forward_kv`` is the bf16 call with Sq queries against Sk keys
-(``fa_fwd_kv``); ``merge`` combines results over disjoint key sets
-(``fa_merge``).  torch only provides device memory and the stream; the computation is
-entirely in the library's HIP kernels.
+stream (or the stream passed).  ``forward_kv`` is the bf16 call with Sq queries
+against Sk keys (``fa_fwd_kv``); ``merge`` combines results over disjoint key
+sets (``fa_merge``); ``backward`` gives the gradients (``fa_bwd``).  torch only
+provides device memory and the stream; the computation is entirely in the
+library's HIP kernels.  Tensors allocated here are allocated on the stream the
+kernels run on, so torch's caching allocator orders their reuse after them.
 """
 
 from __future__ import annotations
@@ -42,6 +44,11 @@ __all__ = ["forward", "forward_kv", "merge", "backward", "fa_fwd", "fa_fwd_f32",
            "fa_merge", "fa_bwd", "fa_fwd_plan", "load", "status_str", "FAError"]
 
 
+def _stream(stream, device):
+    import torch
+    return stream if stream is not None else torch.cuda.current_stream(device)
+
+
 def forward(q, k, v, causal: bool = True, scale: Optional[float] = None,
             out=None, lse=None, stream=None) -> Tuple[object, object]:
     """Attention forward on torch tensors; returns (O, LSE).
@@ -66,26 +73,22 @@ def forward(q, k, v, causal: bool = True, scale: Optional[float] = None,
     B, H, S, D = (int(x) for x in q.shape)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    s = _stream(stream, q.device)
+    with torch.cuda.stream(s):
+        if out is None:
+            out = torch.empty_like(q)
+        if lse is None:
+            lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
     if out.dtype != q.dtype or tuple(out.shape) != (B, H, S, D) or not out.is_contiguous():
         raise ValueError("out must be a contiguous [B,H,S,D] tensor of the input dtype")
     if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, S) or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [B,H,S] tensor")
-    s = stream if stream is not None else torch.cuda.current_stream(q.device)
     fn = fa_fwd if q.dtype == torch.bfloat16 else fa_fwd_f32
     st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
             B, H, S, D, int(bool(causal)), float(scale), s.cuda_stream)
     if st != FA_OK:
         raise FAError(st, fn.__name__)
     return out, lse
-
-
-def _stream(stream, device):
-    import torch
-    return stream if stream is not None else torch.cuda.current_stream(device)
 
 
 def forward_kv(q, k, v, causal: bool = True, scale: Optional[float] = None,
@@ -109,15 +112,16 @@ def forward_kv(q, k, v, causal: bool = True, scale: Optional[float] = None,
         raise ValueError("q, k, v must be contiguous")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    s = _stream(stream, q.device)
+    with torch.cuda.stream(s):
+        if out is None:
+            out = torch.empty_like(q)
+        if lse is None:
+            lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
     if out.dtype != q.dtype or tuple(out.shape) != (B, H, Sq, D) or not out.is_contiguous():
         raise ValueError("out must be a contiguous bf16 [B,H,Sq,D] tensor")
     if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Sq) or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [B,H,Sq] tensor")
-    s = _stream(stream, q.device)
     st = fa_fwd_kv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                    B, H, Sq, Sk, D, int(bool(causal)), float(scale), s.cuda_stream)
     if st != FA_OK:
@@ -139,15 +143,16 @@ def merge(o_parts, lse_parts, out=None, lse=None, stream=None) -> Tuple[object, 
     if not (o_parts.is_contiguous() and lse_parts.is_contiguous()):
         raise ValueError("o_parts and lse_parts must be contiguous")
     G, B, H, S, D = (int(x) for x in o_parts.shape)
-    if out is None:
-        out = torch.empty((B, H, S, D), dtype=torch.bfloat16, device=o_parts.device)
-    if lse is None:
-        lse = torch.empty((B, H, S), dtype=torch.float32, device=o_parts.device)
+    s = _stream(stream, o_parts.device)
+    with torch.cuda.stream(s):
+        if out is None:
+            out = torch.empty((B, H, S, D), dtype=torch.bfloat16, device=o_parts.device)
+        if lse is None:
+            lse = torch.empty((B, H, S), dtype=torch.float32, device=o_parts.device)
     if out.dtype != torch.bfloat16 or tuple(out.shape) != (B, H, S, D) or not out.is_contiguous():
         raise ValueError("out must be a contiguous bf16 [B,H,S,D] tensor")
     if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, S) or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [B,H,S] tensor")
-    s = _stream(stream, o_parts.device)
     st = fa_merge(o_parts.data_ptr(), lse_parts.data_ptr(), G, B, H, S, D, out.data_ptr(),
                   lse.data_ptr(), s.cuda_stream)
     if st != FA_OK:
@@ -161,7 +166,8 @@ def backward(q, k, v, o, lse, dout, causal: bool = True, scale: Optional[float] 
 
     q, k, v, o, dout: bf16 [B, H, S, D]; lse: float32 [B, H, S] (the forward's
     outputs o and lse, same causal and scale).  The Delta buffer the kernels
-    need is allocated here with torch and discarded."""
+    need is allocated here with torch, on the stream the kernels run on, and
+    released when the call returns (the allocator reuses it only after them)."""
     import torch
 
     ts = (q, k, v, o, dout)
@@ -178,9 +184,10 @@ def backward(q, k, v, o, lse, dout, causal: bool = True, scale: Optional[float] 
         raise ValueError("inputs must be contiguous")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    delta = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
     s = _stream(stream, q.device)
+    with torch.cuda.stream(s):
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        delta = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
     st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
                 lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
                 B, H, S, D, int(bool(causal)), float(scale), s.cuda_stream)

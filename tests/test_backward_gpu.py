@@ -121,3 +121,24 @@ def test_single_key_closed_form():
         _, _, dq, dk, dv = run_backward(q, k, v, do, causal, 1 / math.sqrt(D))
         assert torch.equal(dv, do)
         assert dq.abs().max().item() <= 1e-3 and dk.abs().max().item() <= 1e-3
+
+
+def test_backward_on_a_side_stream_matches_current_stream():
+    # The Delta buffer is released when backward() returns; it must be
+    # allocated on the stream the kernels run on, so that allocations made
+    # meanwhile on the current stream cannot take its memory.
+    B, H, S, D = 1, 8, 2048, 128
+    q, k, v = (t.cuda() for t in wl.make_qkv(B, H, S, D, torch.bfloat16, seed=19000))
+    do = _dout(B, H, S, D, 19001).cuda()
+    o, lse = fa.forward(q, k, v, causal=True)
+    ref = fa.backward(q, k, v, o, lse, do, causal=True)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    got = fa.backward(q, k, v, o, lse, do, causal=True, stream=side)
+    churn = [torch.full((B, H, S), float("nan"), dtype=torch.float32, device="cuda")
+             for _ in range(16)]
+    torch.cuda.synchronize()
+    del churn
+    for name, a, b in zip(("dq", "dk", "dv"), got, ref):
+        assert torch.equal(a, b), name
