@@ -1,7 +1,7 @@
 """ctypes binding of the C ABI declared in include/fa.h.
 
-Argument marshalling only: every step of the attention forward runs in the HIP
-kernels of libfa_mi355x.so.  There is no fallback of any kind: if the library
+Argument marshalling only: every step of the attention forward, the merge and
+the backward runs in the HIP kernels of libfa_mi355x.so.  There is no fallback of any kind: if the library
 is missing or cannot be loaded, every call raises.
 """
 
