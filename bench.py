@@ -5,7 +5,8 @@ One step = one call of fa_fwd over the whole workload (inputs resident in HBM
 before timing starts).  Default workload: causal bf16 attention, B=1 H=32
 S=16384 D=128 (the long-sequence causal shape with S >= 4096 and D = 128).
 Prints ONE JSON line on stdout; a per-workload table goes to stderr with
---all.
+--all.  The line's "secondary" object adds, outside `value`, the queries-
+against-a-prefix path (prefill, decode), the merge and the backward pass.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                   [--all] [--no-cpu-baseline] [--copy-calibration]
@@ -284,7 +285,7 @@ def main():
     ap.add_argument("--all", action="store_true", help="also time every workload (stderr)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true",
-                    help="skip the Sq != Sk and merge workloads")
+                    help="skip the secondary figures (Sq != Sk, merge, backward)")
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the cold-cache launches (profiling runs count warm launches only)")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -388,7 +389,8 @@ def main():
         },
         "cold": cold,
         "cpu_baseline": cpu,
-        # not part of `value`: the Sq != Sk path and the merge on their own workloads
+        # not part of `value`: the Sq != Sk path, the merge and the backward pass,
+        # each on its own workloads
         "secondary": secondary,
     }
     if rank == 0:
