@@ -338,9 +338,10 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dkdv_kernel(
       };
       // The products of a 16-query chunk follow the chunk's weights, and
       // S(t+1), dP(t+1) are split around them, so the matrix cores always
-      // have independent work while the weights form.  (Pinning this order
-      // with scheduling barriers made the kernel slower: with one wavefront
-      // per SIMD the compiler's own interleave hides more of the LDS latency.)
+      // have independent work while the weights form.  The compiler's
+      // MFMA/LDS interleave strategy 1 orders the region (measured: 3-6 %
+      // faster than its default order; pinning the order with scheduling
+      // group barriers, as the forward does, was 7 % slower).
 #pragma unroll
       for (int qb = 0; qb < C::KB; ++qb) {
         qk_block<C>(s_out[qb], qr_n, kf, k_off, qb);
@@ -353,6 +354,7 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dkdv_kernel(
           tr_chunk<C, NB>(dk_acc, qt, dsq[2 * qb + half], v_off, 2 * qb + half, part);  // dK^T += q^T dS
         }
       }
+      __builtin_amdgcn_iglp_opt(1);
     } else if (t + 1 < nt && live(t + 1)) {
       // the wave's first tile is the next one: only S(t+1), dP(t+1)
 #pragma unroll
@@ -534,6 +536,8 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 2 : 1) void fa_bwd_dq_kern
           dsf[2 * kb + (r >> 3)][r & 7] = (__bf16)(p * (dp[kb][r] - delta));
         }
       tr_product_u<C>(acc, kr, dsf, v_off, v_hi);  // dq^T += K^T dS^T
+      // compiler MFMA/LDS interleave strategy 1 (measured: 0.5-2 % faster)
+      __builtin_amdgcn_iglp_opt(1);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
