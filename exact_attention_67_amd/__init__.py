@@ -34,6 +34,7 @@ from ._lib import (  # noqa: F401
     fa_bwd,
     fa_fwd_f32,
     fa_fwd_kv,
+    fa_fwd_kv_plan,
     fa_fwd_plan,
     fa_merge,
     load,
@@ -41,7 +42,8 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = ["forward", "forward_kv", "merge", "backward", "fa_fwd", "fa_fwd_f32", "fa_fwd_kv",
-           "fa_merge", "fa_bwd", "fa_fwd_plan", "load", "status_str", "FAError"]
+           "fa_merge", "fa_bwd", "fa_fwd_plan", "fa_fwd_kv_plan", "load", "status_str",
+           "FAError"]
 
 
 def _stream(stream, device):

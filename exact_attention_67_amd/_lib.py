@@ -27,7 +27,7 @@ FA_ERR_ALIAS = 7
 FA_ERR_LAUNCH = 8
 
 EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_kv", "fa_merge", "fa_bwd", "fa_fwd_plan",
-           "fa_status_str", "fa_abi_version")
+           "fa_fwd_kv_plan", "fa_status_str", "fa_abi_version")
 ABI_VERSION = 1
 
 _lock = threading.Lock()
@@ -58,6 +58,8 @@ def _declare(lib: ctypes.CDLL) -> None:
     ip = ctypes.POINTER(i)
     lib.fa_fwd_plan.argtypes = [i, i, i, i, i, i, ip, ip, ip, ip]
     lib.fa_fwd_plan.restype = i
+    lib.fa_fwd_kv_plan.argtypes = [i, i, i, i, i, i, ip, ip, ip, ip]
+    lib.fa_fwd_kv_plan.restype = i
     lib.fa_status_str.argtypes = [i]
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_abi_version.argtypes = []
@@ -127,5 +129,17 @@ def fa_fwd_plan(B: int, H: int, S: int, D: int, causal: int, elem_bytes: int) ->
     st = load().fa_fwd_plan(B, H, S, D, causal, elem_bytes, *[ctypes.byref(x) for x in out])
     if st != FA_OK:
         raise FAError(st, "fa_fwd_plan")
+    return dict(zip(("rows_per_group", "keys_per_tile", "threads", "groups"),
+                    (x.value for x in out)))
+
+
+def fa_fwd_kv_plan(B: int, H: int, Sq: int, Sk: int, D: int, causal: int) -> dict:
+    """Launch shape fa_fwd_kv uses for Sq queries against Sk keys (host-only
+    query).  Returns {rows_per_group, keys_per_tile, threads, groups}; raises
+    FAError."""
+    out = [ctypes.c_int(-1) for _ in range(4)]
+    st = load().fa_fwd_kv_plan(B, H, Sq, Sk, D, causal, *[ctypes.byref(x) for x in out])
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd_kv_plan")
     return dict(zip(("rows_per_group", "keys_per_tile", "threads", "groups"),
                     (x.value for x in out)))

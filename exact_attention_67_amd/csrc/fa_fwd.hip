@@ -1103,4 +1103,17 @@ extern "C" int fa_fwd_plan(int B, int H, int S, int D, int causal, int elem_byte
   return FA_OK;
 }
 
+extern "C" int fa_fwd_kv_plan(int B, int H, int Sq, int Sk, int D, int causal,
+                              int* rows_per_group, int* keys_per_tile, int* threads,
+                              int* groups) {
+  const int st = validate_shape(B, H, Sq, Sk, D, causal, 2);
+  if (st != FA_OK) return st;
+  const LaunchCfg cfg = bf16_config(Sq, Sk, D, causal != 0, B * H);
+  if (rows_per_group) *rows_per_group = kRowsPerWave * cfg.waves;
+  if (keys_per_tile) *keys_per_tile = cfg.bc;
+  if (threads) *threads = 64 * cfg.waves;
+  if (groups) *groups = (int)cfg.grid;
+  return FA_OK;
+}
+
 extern "C" int fa_abi_version(void) { return 1; }

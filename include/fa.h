@@ -168,13 +168,25 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
  *   keys_per_tile  : keys per K/V tile staged in on-chip memory
  *   threads        : threads per workgroup
  *   groups         : workgroups in the grid
- * For fa_fwd_kv pass S = Sq (the grid depends on the query rows only).
- * Outputs are host pointers; each may be NULL.  Returns FA_ERR_SHAPE,
- * FA_ERR_HEADDIM or FA_ERR_CAUSAL where fa_fwd would (FA_ERR_SHAPE also for
- * elem_bytes other than 2 or 4), leaving the outputs untouched; else FA_OK.
+ * For fa_fwd_kv use fa_fwd_kv_plan (with the causal mask the choice also
+ * depends on the key count).  Outputs are host pointers; each may be NULL.
+ * Returns FA_ERR_SHAPE, FA_ERR_HEADDIM or FA_ERR_CAUSAL where fa_fwd would
+ * (FA_ERR_SHAPE also for elem_bytes other than 2 or 4), leaving the outputs
+ * untouched; else FA_OK.
  */
 int fa_fwd_plan(int B, int H, int S, int D, int causal, int elem_bytes,
                 int* rows_per_group, int* keys_per_tile, int* threads, int* groups);
+
+/*
+ * fa_fwd_kv_plan -- the launch shape fa_fwd_kv uses for Sq queries against
+ * Sk keys (bf16), computed on the host without any HIP call; outputs as for
+ * fa_fwd_plan.  Queries behind a key prefix at least as long as themselves
+ * have work-balanced query tiles, which changes the workgroup choice.
+ * Returns the status fa_fwd_kv would return for these sizes, leaving the
+ * outputs untouched on error; else FA_OK.
+ */
+int fa_fwd_kv_plan(int B, int H, int Sq, int Sk, int D, int causal,
+                   int* rows_per_group, int* keys_per_tile, int* threads, int* groups);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa_status_str(int status);

@@ -193,6 +193,26 @@ def test_plan_covers_every_query_row(B, H, S, D, causal, eb):
     assert per_head * rows >= S > (per_head - 1) * rows     # every row once, no empty tile
 
 
+def test_kv_plan_workgroup_choice():
+    # causal, square sequence: 300 tiles of 256 rows are fewer than two per CU
+    assert fa.fa_fwd_kv_plan(1, 300, 200, 200, 128, 1)["rows_per_group"] == 128
+    # the same queries behind 300 more keys: tiles within 4/3 of the mean
+    # length, one per CU is enough
+    p = fa.fa_fwd_kv_plan(1, 300, 200, 500, 128, 1)
+    assert p["rows_per_group"] == 256 and p["groups"] == 300 and p["threads"] == 512
+    # a prefix shorter than the queries keeps the square rule
+    assert fa.fa_fwd_kv_plan(1, 300, 200, 399, 128, 1)["rows_per_group"] == 128
+    # no mask: one per CU
+    assert fa.fa_fwd_kv_plan(1, 300, 200, 200, 128, 0)["rows_per_group"] == 256
+    # square sizes agree with fa_fwd_plan
+    for B, H, S, D, c in ((1, 32, 16384, 128, 1), (1, 16, 4096, 128, 1), (2, 8, 999, 256, 0)):
+        assert fa.fa_fwd_kv_plan(B, H, S, S, D, c) == fa.fa_fwd_plan(B, H, S, D, c, 2)
+    with pytest.raises(fa.FAError):
+        fa.fa_fwd_kv_plan(1, 1, 0, 10, 128, 1)
+    with pytest.raises(fa.FAError):
+        fa.fa_fwd_kv_plan(1, 1, 10, 10, 96, 1)
+
+
 def test_plan_workgroup_choice():
     # D = 128: 256-row workgroups once the grid still has >= 2 per CU (causal)
     # or >= 1 per CU (no mask); 128-row workgroups otherwise and for D != 128.

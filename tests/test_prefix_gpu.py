@@ -120,6 +120,7 @@ def test_fwd_kv_prefix_single_round_of_256_row_workgroups():
     # queries behind a key prefix at least as long as themselves have nearly
     # equal tiles: 256-row workgroups already at one per CU (300 of them here)
     B, H, Sq, Sk, D = 1, 300, 200, 500, 128
+    assert fa.fa_fwd_kv_plan(B, H, Sq, Sk, D, 1)["rows_per_group"] == 256
     q, k, v = _qkv(B, H, Sq, Sk, D, seed=6500)
     s = _scale(D)
     o, lse = fa.forward_kv(q.cuda(), k.cuda(), v.cuda(), causal=True, scale=s)
