@@ -330,3 +330,16 @@ def test_generator_statistics_sane():
     q, k, v = wl.make_qkv(1, 2, 512, 64, torch.float32, 3)
     _, l = orc.attention_reference(q, k, v, False, 1 / 8)
     assert abs(l.mean().item() - (math.log(512) + 0.5)) < 0.1
+
+
+def test_default_scale_closed_forms():
+    # 1/sqrt(head_dim) is a power of two at D = 64 and D = 256, and at D = 128
+    # its square times D is 1; a call without a scale uses it
+    assert orc.default_scale(64) == 0.125
+    assert orc.default_scale(256) == 0.0625
+    assert abs(orc.default_scale(128) ** 2 * 128 - 1.0) < 1e-15
+    g = torch.Generator().manual_seed(3)
+    q, k, v = (torch.randn((1, 2, 9, 64), generator=g, dtype=torch.float64) for _ in range(3))
+    o_default, l_default = orc.attention_reference(q, k, v, True)
+    o_eighth, l_eighth = orc.attention_reference(q, k, v, True, 0.125)
+    assert torch.equal(o_default, o_eighth) and torch.equal(l_default, l_eighth)
