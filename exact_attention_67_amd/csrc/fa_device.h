@@ -44,8 +44,10 @@ __device__ __forceinline__ int xcd_logical_index(int i, int n) {
 }
 
 // Logical index -> (bh, query tile).  Heads are taken in groups of
-// `group_heads`; inside a group the tiles of its heads are interleaved, and
-// when causal the heaviest (last) query tiles come first.
+// `group_heads`.  Causal: inside a group the tiles of its heads are
+// interleaved, heaviest (last) query tiles first, so that every round of
+// workgroups holds a mix of long and short ones.  Without the mask all tiles
+// are equally long and the group is walked head by head.
 template <bool CAUSAL>
 __device__ __forceinline__ void decode_tile(int L, int nq, int bh_total, int group_heads,
                                             int& bh, int& qt) {
@@ -54,9 +56,15 @@ __device__ __forceinline__ void decode_tile(int L, int nq, int bh_total, int gro
   const int r = L - grp * gsize;
   const int left = bh_total - grp * group_heads;
   const int hin = left < group_heads ? left : group_heads;
-  bh = grp * group_heads + r % hin;
-  const int rank = r / hin;
-  qt = CAUSAL ? (nq - 1 - rank) : rank;
+  if (CAUSAL) {
+    bh = grp * group_heads + r % hin;
+    qt = nq - 1 - r / hin;
+  } else {
+    // equal-length tiles: head-major, so that the workgroups running at the
+    // same time on an XCD stream the same head's K/V through its L2
+    bh = grp * group_heads + r / nq;
+    qt = r % nq;
+  }
 }
 
 // ----------------------------------------------------------------------------
