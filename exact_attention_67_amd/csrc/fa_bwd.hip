@@ -81,8 +81,7 @@ __global__ __launch_bounds__(256) void fa_bwd_delta_kernel(const uint16_t* __res
 // src[min(row0 + l, S - 1)].
 __device__ __forceinline__ void issue_rowvec(const float* __restrict__ src, lds_u8* dst, int row0,
                                              int S, int lane) {
-  const void* gp = src + min(row0 + lane, S - 1);
-  __builtin_amdgcn_global_load_lds(gp, dst, 4, 0, 0);
+  lds_dma<4>(src, (uint32_t)min(row0 + lane, S - 1) * 4u, dst);
 }
 
 typedef __attribute__((address_space(3))) float lds_f32;

@@ -160,6 +160,33 @@ __device__ __forceinline__ void tile_offsets(int* off, int* row, int part, int l
   }
 }
 
+// Buffer-resource word 3 for raw (untyped) buffer loads on gfx9-family GPUs.
+constexpr int kRawBufferWord3 = 0x00020000;
+
+// Asynchronous global -> LDS copy of BYTES per lane: lane l's bytes at
+// base + boff land in LDS at dst + BYTES * l.  Issued as a buffer load with
+// the LDS bit: it is tracked by the vector-memory counter only, so the
+// compiler keeps exact LDS-counter waits for the operand reads that run while
+// copies are in flight.  (For the global-segment form of the same copy the
+// compiler assumes it may be pending on the LDS counter too and turns every
+// such wait into a wait for all outstanding LDS operations.)  `base` is made
+// wave-uniform (scalar registers); `boff` is the per-lane byte offset.
+template <int BYTES>
+__device__ __forceinline__ void lds_dma(const void* base, uint32_t boff, lds_u8* dst) {
+  const uint64_t b64 = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b64);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b64 >> 32));
+  void* p = (void*)(((uint64_t)hi << 32) | lo);
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(p, (short)0, -1, kRawBufferWord3);
+  auto* d = (__attribute__((address_space(3))) void*)dst;
+  static_assert(BYTES == 16 || BYTES == 4, "copy size per lane");
+  if constexpr (BYTES == 16)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, d, 16, boff, 0, 0, 0);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, d, 4, boff, 0, 0, 0);
+}
+
 // Asynchronous global -> LDS copy of one K or V tile.  Share `part` of the
 // copy, issued by one wave, is LOADS_PER_WAVE transfers of 1 KiB, lane l
 // filling bytes 16l .. 16l+15 (a wave-uniform base address plus a per-lane
@@ -178,18 +205,13 @@ __device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ head_src
   lds_u8* lds = dst + part * (C::LOADS_PER_WAVE * 1024);
   if (k0 + C::BC <= S) {
 #pragma unroll
-    for (int u = 0; u < C::LOADS_PER_WAVE; ++u) {
-      const void* gp = base + (uint32_t)(off[u] * 2);
-      lds_u8* lp = lds + u * 1024;
-      __builtin_amdgcn_global_load_lds(gp, lp, 16, 0, 0);
-    }
+    for (int u = 0; u < C::LOADS_PER_WAVE; ++u)
+      lds_dma<16>(base, (uint32_t)(off[u] * 2), lds + u * 1024);
   } else {
 #pragma unroll
     for (int u = 0; u < C::LOADS_PER_WAVE; ++u) {
       const int o = off[u] - (row[u] - min(row[u], S - 1 - k0)) * C::D;
-      const void* gp = base + (uint32_t)(o * 2);
-      lds_u8* lp = lds + u * 1024;
-      __builtin_amdgcn_global_load_lds(gp, lp, 16, 0, 0);
+      lds_dma<16>(base, (uint32_t)(o * 2), lds + u * 1024);
     }
   }
 }

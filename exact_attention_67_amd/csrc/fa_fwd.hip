@@ -334,8 +334,7 @@ __device__ __forceinline__ void tile_src(const uint16_t* __restrict__ head_src, 
 
 // One 1 KiB piece (16 bytes per lane) of a tile copy into LDS.
 __device__ __forceinline__ void copy_piece(const char* base, int boff, lds_u8* dst) {
-  const void* gp = base + (uint32_t)boff;
-  __builtin_amdgcn_global_load_lds(gp, dst, 16, 0, 0);
+  lds_dma<16>(base, (uint32_t)boff, dst);
 }
 
 // A workgroup barrier that waits for nothing by itself (copies in flight stay
