@@ -95,6 +95,30 @@ def test_backward_larger(D):
         check_grads((dq, dk, dv), ref, f"bwd 2x4x1024 D={D} causal={causal}")
 
 
+def test_backward_tensors_beyond_4gib():
+    # Every tensor larger than 4 GiB (heads at the end lie more than 2^32
+    # bytes past the base); gradients of the first head and of the last one
+    # against the oracle on those heads (inputs drawn on the GPU from a seeded
+    # generator, the two heads copied back).
+    S, D, causal = 1000, 128, True
+    heads = (1 << 32) // (S * D * 2) + 3
+    B, H = 2, (heads + 1) // 2
+    assert B * H * S * D * 2 > (1 << 32)
+    g = torch.Generator(device="cuda").manual_seed(19500)
+    q, k, v, do = (torch.randn((B, H, S, D), generator=g, device="cuda", dtype=torch.bfloat16)
+                   for _ in range(4))
+    scale = float(torch.tensor(1 / math.sqrt(D), dtype=torch.float32))
+    o, lse = fa.forward(q, k, v, causal=causal, scale=scale)
+    dq, dk, dv = fa.backward(q, k, v, o, lse, do, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    for b, h in [(0, 0), (B - 1, H - 1)]:
+        sl = lambda t: t[b:b + 1, h:h + 1].cpu()
+        ref = bwd.attention_backward(sl(q), sl(k), sl(v), sl(do), causal, scale)
+        check_grads((sl(dq), sl(dk), sl(dv)), ref, f"bwd >4GiB b={b} h={h}")
+    del q, k, v, do, o, lse, dq, dk, dv
+    torch.cuda.empty_cache()
+
+
 def test_delta_buffer_is_rowsum():
     B, H, S, D = 1, 2, 200, 128
     q, k, v = (t.cuda() for t in wl.make_qkv(B, H, S, D, torch.bfloat16, seed=15000))

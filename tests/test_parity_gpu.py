@@ -175,6 +175,36 @@ def test_long_sequence_sampled_rows(D, causal):
               l_ref.unsqueeze(0), torch.bfloat16, f"long S={S} D={D} causal={causal} h={h}")
 
 
+@pytest.mark.parametrize("D,causal", [(64, False), (128, True), (256, True)])
+def test_tensors_beyond_4gib(D, causal):
+    # Every tensor is larger than 4 GiB, so the heads at its end lie more than
+    # 2^32 bytes past its base: the per-head and per-tile base addresses of
+    # the K/V copies, the Q loads and the O/LSE stores are 64-bit while the
+    # per-lane offsets are 32-bit.  Ragged S; sampled rows of the first head
+    # and of the last two, against the oracle (inputs drawn on the GPU from a
+    # seeded generator, the sampled heads copied back for the oracle).
+    S = 1000
+    heads = (1 << 32) // (S * D * 2) + 3
+    B, H = 2, (heads + 1) // 2
+    assert B * H * S * D * 2 > (1 << 32)
+    g = torch.Generator(device="cuda").manual_seed(19000 + D)
+    q, k, v = (torch.randn((B, H, S, D), generator=g, device="cuda", dtype=torch.bfloat16)
+               for _ in range(3))
+    scale = float(torch.tensor(1 / math.sqrt(D), dtype=torch.float32))
+    say(f"tensors beyond 4 GiB: B={B} H={H} S={S} D={D} causal={causal}")
+    o, lse = fa.forward(q, k, v, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    rows = [0, 1, 127, 128, 255, 256, 511, 777, 998, 999]
+    for b, h in [(0, 0), (B - 1, H - 2), (B - 1, H - 1)]:
+        qh, kh, vh = (t[b:b + 1, h:h + 1].cpu() for t in (q, k, v))
+        o_ref, l_ref = orc.attention_rows(qh, kh, vh, causal, scale, 0, 0, rows)
+        check(o[b, h, rows].cpu().unsqueeze(0), lse[b, h, rows].cpu().unsqueeze(0),
+              o_ref.unsqueeze(0), l_ref.unsqueeze(0), torch.bfloat16,
+              f">4GiB D={D} causal={causal} b={b} h={h}")
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("D", [64, 128, 256])
 def test_zero_keys_give_prefix_means(D):
     S = 200
