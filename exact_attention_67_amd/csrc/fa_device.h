@@ -97,8 +97,7 @@ struct BfCfg {
   static constexpr int RC = D / 8;                     // 16-byte chunks per row
   static constexpr int ROWS_PER_LOAD = 64 / RC;        // rows per 1 KiB wave load
   // Waves that issue the tile copies: all of a 4-wave workgroup; in an 8-wave
-  // workgroup only waves 0..3 (one per SIMD), which leaves their SIMD
-  // partners free to start on the matrix cores right after the barrier.
+  // workgroup four of them, one per SIMD.
   static constexpr int COPY_WAVES = WAVES == 8 ? 4 : WAVES;
   static constexpr int LOADS_PER_WAVE = TILE_BYTES / 1024 / COPY_WAVES;  // per tensor
   // VALU instructions the schedule places after each MFMA of a tile.

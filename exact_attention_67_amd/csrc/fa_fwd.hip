@@ -109,8 +109,11 @@ __global__ __launch_bounds__(64 * WAVES, D <= 128 ? 2 : 1) void fa_fwd_bf16_kern
 
   int koff[C::LOADS_PER_WAVE], krow[C::LOADS_PER_WAVE];
   int voff[C::LOADS_PER_WAVE], vrow[C::LOADS_PER_WAVE];
-  const bool copier = wave < C::COPY_WAVES;
-  const int cw = copier ? wave : 0;  // this wave's share of each tile copy
+  // Copy waves: the last COPY_WAVES waves (all of a 4-wave workgroup; waves
+  // 4..7, one per SIMD, of an 8-wave one, which otherwise finish each tile
+  // later than their SIMD partners 0..3).
+  const bool copier = wave >= WAVES - C::COPY_WAVES;
+  const int cw = copier ? wave - (WAVES - C::COPY_WAVES) : 0;  // this wave's share of each copy
   tile_offsets<C, false>(koff, krow, cw, lane);
   tile_offsets<C, true>(voff, vrow, cw, lane);
 
