@@ -21,6 +21,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
@@ -80,6 +81,9 @@ typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 // A row's reference max is only raised when its running max exceeds it by
 // more than this many powers of two, so softmax weights stay <= 2^8.
 constexpr float kRescaleThreshold = 8.0f;
+// Largest sum of one lane's softmax weights in a tile (32 keys) that the
+// kernels accept without moving the row's reference max.
+constexpr float kRowSumLimit = 4096.0f;
 
 template <int D_, int BC_, int WAVES_>
 struct BfCfg {
@@ -171,7 +175,8 @@ constexpr int kRawBufferWord3 = 0x00020000;
 // such wait into a wait for all outstanding LDS operations.)  `base` is made
 // wave-uniform (scalar registers); `boff` is the per-lane byte offset.
 template <int BYTES>
-__device__ __forceinline__ void lds_dma(const void* base, uint32_t boff, lds_u8* dst) {
+__device__ __forceinline__ void lds_dma(const void* base, uint32_t boff, lds_u8* dst,
+                                        int soff = 0) {
   const uint64_t b64 = (uint64_t)base;
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b64);
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b64 >> 32));
@@ -181,9 +186,9 @@ __device__ __forceinline__ void lds_dma(const void* base, uint32_t boff, lds_u8*
   auto* d = (__attribute__((address_space(3))) void*)dst;
   static_assert(BYTES == 16 || BYTES == 4, "copy size per lane");
   if constexpr (BYTES == 16)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, d, 16, boff, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, d, 16, boff, soff, 0, 0);
   else
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, d, 4, boff, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, d, 4, boff, soff, 0, 0);
 }
 
 // Asynchronous global -> LDS copy of one K or V tile.  Share `part` of the
@@ -211,6 +216,68 @@ __device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ head_src
     for (int u = 0; u < C::LOADS_PER_WAVE; ++u) {
       const int o = off[u] - (row[u] - min(row[u], S - 1 - k0)) * C::D;
       lds_dma<16>(base, (uint32_t)(o * 2), lds + u * 1024);
+    }
+  }
+}
+
+// Compact per-lane state of the tile copies (D = 64 and 128, where a tile
+// row is at most 256 bytes).  This lane's 16 bytes of piece 0 of the wave's
+// share sit in tile row row0; piece u holds rows row0 + u * ROWS_PER_LOAD,
+// 1 KiB further on in both memories.  Those rows have row0's V swizzle, and a
+// K swizzle that differs from row0's by an XOR of 4u, so a piece's offsets
+// follow from piece 0's with a scalar offset (and, for K, one XOR).
+struct CopyLanes {
+  int krow;   // K: byte offset of row row0 in the tile
+  int kch;    // K: byte offset, within the row, of this lane's chunk in piece 0
+  int vbyte;  // V: byte offset of this lane's 16 bytes in piece 0
+};
+
+template <class C>
+__device__ __forceinline__ CopyLanes copy_lanes(int part, int lane) {
+  // kswz(r) = (r / ROWS_PER_LINE) mod P, P = CH_PER_LINE / ROWS_PER_LINE: the
+  // share's first row is a multiple of P lines, a lane's row within piece 0
+  // adds < 4 lines, and piece u adds 4u lines with 4u + 3 < P.
+  constexpr int P = C::CH_PER_LINE / C::ROWS_PER_LINE;
+  static_assert(C::ROW_BYTES <= 256 && C::ROWS_PER_LOAD == 4 * C::ROWS_PER_LINE &&
+                    (C::LOADS_PER_WAVE * C::ROWS_PER_LOAD / C::ROWS_PER_LINE) % P == 0 &&
+                    4 * C::LOADS_PER_WAVE <= P,
+                "piece u's K swizzle must be piece 0's XOR 4u");
+  const int row0 = part * C::LOADS_PER_WAVE * C::ROWS_PER_LOAD + lane / C::RC;
+  CopyLanes cl;
+  cl.krow = row0 * C::ROW_BYTES;
+  cl.kch = ((lane % C::RC) ^ kswz<C>(row0)) << 4;
+  cl.vbyte = row0 * C::ROW_BYTES + (((lane % C::RC) ^ vswz<C>(row0)) << 4);
+  return cl;
+}
+
+// Asynchronous global -> LDS copy of one K (IS_V false) or V tile with the
+// compact lane state: share `part`, LOADS_PER_WAVE pieces of 1 KiB.  In the
+// last (partial) tile, rows past the sequence end are clamped to the last
+// row: finite data whose keys are masked.
+template <class C, bool IS_V>
+__device__ __forceinline__ void copy_tile(const uint16_t* __restrict__ head_src, lds_u8* dst,
+                                          int k0, int S, int part, int lane,
+                                          const CopyLanes& cl) {
+  const uint64_t b64 = (uint64_t)(head_src + (size_t)k0 * C::D);
+  const uint32_t b_lo = __builtin_amdgcn_readfirstlane((uint32_t)b64);
+  const uint32_t b_hi = __builtin_amdgcn_readfirstlane((uint32_t)(b64 >> 32));
+  const char* base = (const char*)(((uint64_t)b_hi << 32) | b_lo);
+  lds_u8* lds = dst + part * (C::LOADS_PER_WAVE * 1024);
+  if (k0 + C::BC <= S) {
+#pragma unroll
+    for (int u = 0; u < C::LOADS_PER_WAVE; ++u) {
+      const int o = IS_V ? cl.vbyte : cl.krow + (cl.kch ^ (64 * u));
+      lds_dma<16>(base, (uint32_t)o, lds + u * 1024, 1024 * u);
+    }
+  } else {
+    const int row0 = part * C::LOADS_PER_WAVE * C::ROWS_PER_LOAD + lane / C::RC;
+    const int chunk = IS_V ? cl.vbyte - cl.krow : cl.kch;  // piece 0's chunk byte offset
+#pragma unroll
+    for (int u = 0; u < C::LOADS_PER_WAVE; ++u) {
+      const int r = row0 + u * C::ROWS_PER_LOAD;
+      const int src_row = min(r, S - 1 - k0);
+      const int o = src_row * C::ROW_BYTES + (IS_V ? chunk : (chunk ^ (64 * u)));
+      lds_dma<16>(base, (uint32_t)o, lds + u * 1024);
     }
   }
 }

@@ -30,11 +30,15 @@
 //    LDS read (two ds_read_b64_tr_b16 per MFMA).
 //  * LDS rows are XOR-swizzled in 16-byte units so the MFMA operand reads are
 //    free of bank conflicts on the 64-bank LDS.
-//  * exp2 with the scale folded into one FMA per score.  The reference max of
-//    a row is raised only when the row's max exceeds it by more than 2^8, so
-//    the rescale of the O accumulator (a wave-uniform branch) runs on few
-//    tiles; weights stay <= 2^8, and O is normalised by the sum of the bf16
-//    weights that multiplied V.
+//  * exp2 with the scale folded into one FMA per score.  A row's reference
+//    max is raised only when the weights of a tile would grow too large (D <=
+//    128: a lane's sum of weights in the tile above 2^12, found after the
+//    weights are formed, with P*V deferred by one tile so that it only ever
+//    sees checked weights; D = 256: the tile's row max above the reference by
+//    more than 8 powers of two), so the rescale of the O accumulator (a
+//    wave-uniform branch) runs on few tiles.  O is normalised by the sum of
+//    the bf16 weights that multiplied V (for D <= 128 formed on the matrix
+//    cores by a 16x16x32 product with a 0/1 operand).
 //  * The 1-D grid is decoded XCD-aware (the 8 XCDs receive workgroups round-
 //    robin; consecutive logical tiles of the same heads are kept on one XCD so
 //    they share its L2) and, when causal, heaviest query tiles first.
@@ -47,6 +51,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fa.h"
 #include "fa_device.h"
 
@@ -55,11 +61,80 @@ namespace {
 constexpr int kWaves = 4;                   // float32 kernel: wavefronts per workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBr = kRowsPerWave * kWaves;  // float32 kernel: query rows per workgroup
+#ifndef FA_MFMA_SUM
+#define FA_MFMA_SUM 1
+#endif
+constexpr bool kMfmaSum = FA_MFMA_SUM != 0;  // bf16-weight sums on the matrix cores
 
-// Two waves per SIMD up to D = 128 (two 4-wave or one 8-wave workgroup per
-// CU); D = 256 needs the full register file.
-template <int D, int BC, int WAVES, bool CAUSAL>
-__global__ __launch_bounds__(64 * WAVES, D <= 128 ? 2 : 1) void fa_fwd_bf16_kernel(
+// sched_group_barrier with a compile-time count; nothing when the count is 0.
+template <int MASK, int N>
+__device__ __forceinline__ void sched_group() {
+  if constexpr (N > 0) __builtin_amdgcn_sched_group_barrier(MASK, N, 0);
+}
+
+// Fixed instruction order of one full tile step of fa_fwd_bf16_kernel (product
+// I of the step is the I-th MFMA in program order: the bf16-weight sums when
+// MFMA_SUM, then the P*V products, then the S products).  Each product is
+// followed by the operand reads of the product kLead places later (two
+// transposing V reads for a P*V product, one K read for an S product) and by
+// its share of the step's exponentials and other vector instructions.
+#ifndef FA_READ_LEAD
+#define FA_READ_LEAD 3
+#endif
+template <class C, bool MFMA_SUM, int N>
+struct StepOrder {
+  static constexpr int kLead = FA_READ_LEAD;
+  static constexpr int kSum = MFMA_SUM ? C::PCH : 0;
+  static constexpr int kPV = C::DB * C::PCH;
+  // one exponential per score; an FMA and an add per score, a bf16 pack per
+  // pair, and the dot products of the bf16 sums when they are not on the
+  // matrix cores
+  static constexpr int kTrans = C::KB * 16;
+  static constexpr int kValu = C::KB * 16 * 2 + C::KB * 8 + (MFMA_SUM ? 0 : C::PCH * 4);
+  // operand reads issued after product i: those of product i + kLead
+  static constexpr int reads(int i) {
+    const int j = i + kLead - kSum;  // index among the P*V and S products
+    if (j < 0) return 0;
+    if (j < kPV) return 2;
+    return j < N - kSum ? 1 : 0;
+  }
+  // reads of the products that start before any product has issued
+  static constexpr int first_reads() {
+    int n = 0;
+    for (int j = 0; j < kLead - kSum && j < N - kSum; ++j) n += j < kPV ? 2 : 1;
+    return n;
+  }
+  // product i's share of `total` instructions, spread evenly
+  static constexpr int share(int i, int total) { return ((i + 1) * total) / N - (i * total) / N; }
+};
+
+template <class C, bool MFMA_SUM, int... I>
+__device__ __forceinline__ void step_schedule(std::integer_sequence<int, I...>) {
+  using O = StepOrder<C, MFMA_SUM, (int)sizeof...(I)>;
+  sched_group<0x100, O::first_reads()>();
+  ((sched_group<0x008, 1>(), sched_group<0x100, O::reads(I)>(),
+    sched_group<0x200, O::share(I, O::kTrans)>(), sched_group<0x002, O::share(I, O::kValu)>()),
+   ...);
+}
+
+// Two waves per SIMD (two 4-wave or one 8-wave workgroup per CU; D <= 128).
+//
+// Tile step t (one 64-key tile; one workgroup barrier per step):
+//  * the weights of tile t are formed from S(t), computed in step t-1:
+//    p = 2^(s*c - m*c) against the row's reference max m, rounded to bf16;
+//  * O += P(t-1) V(t-1) and the row sums of the bf16 weights of tile t-1 on
+//    the matrix cores (the weights were checked at the end of step t-1);
+//  * S(t+1) = Q K(t+1)^T on the matrix cores.
+// The vector work of the step (one FMA, one exponential, one add per score and
+// one bf16 pack per pair) runs beside the step's 36 matrix instructions.  The
+// row max is not taken per tile: after the weights of tile t are formed, a
+// lane whose sum of weights exceeds kRowSumLimit (or is not finite) sends the
+// wave through a rare path that raises the reference to the tile's max and
+// rescales (weights stay <= kRowSumLimit, so nothing overflows).  The
+// reference is set from the true max of tile 0 before the first step, and it
+// only moves up, so the largest weight of a row is >= 1.
+template <int D, int BC, int WAVES, bool CAUSAL, bool MFMA_SUM>
+__global__ __launch_bounds__(64 * WAVES, 2) void fa_fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
     int Sq, int Sk, int nq, int bh_total, int group_heads, float c) {
@@ -100,28 +175,23 @@ __global__ __launch_bounds__(64 * WAVES, D <= 128 ? 2 : 1) void fa_fwd_bf16_kern
   // The queries are the last Sq positions of the Sk keys' sequence: with the
   // causal mask, query row i sees keys j <= i + kshift (bottom-right
   // alignment; kshift = 0 for self-attention).  Rows before the first key see
-  // nothing (possible when Sq > Sk).
+  // nothing (possible when Sq > Sk).  Every row that sees a key sees key 0.
   const int kshift = Sk - Sq;
   const int kend = CAUSAL ? max(0, min(Sk, q0 + C::BR + kshift)) : Sk;
   const int ntiles = (kend + BC - 1) / BC;
   const int wave_klast = CAUSAL ? min(qw0 + kRowsPerWave - 1 + kshift, Sk - 1) : (Sk - 1);
   const int wave_ntiles = (qw0 < Sq && wave_klast >= 0) ? min(ntiles, wave_klast / BC + 1) : 0;
 
-  int koff[C::LOADS_PER_WAVE], krow[C::LOADS_PER_WAVE];
-  int voff[C::LOADS_PER_WAVE], vrow[C::LOADS_PER_WAVE];
   // Copy waves: the last COPY_WAVES waves (all of a 4-wave workgroup; waves
-  // 4..7, one per SIMD, of an 8-wave one, which otherwise finish each tile
-  // later than their SIMD partners 0..3).
+  // 4..7, one per SIMD, of an 8-wave one).
   const bool copier = wave >= WAVES - C::COPY_WAVES;
   const int cw = copier ? wave - (WAVES - C::COPY_WAVES) : 0;  // this wave's share of each copy
-  tile_offsets<C, false>(koff, krow, cw, lane);
-  tile_offsets<C, true>(voff, vrow, cw, lane);
+  const CopyLanes cl = copy_lanes<C>(cw, lane);
 
-  // The K stream runs one tile ahead of the V stream: K(0), K(1), V(0) now.
+  // K(0) and K(1) now; step t copies K(t+2) and V(t).
   if (copier && ntiles > 0) {
-    issue_tile<C>(Kh, kbuf0, 0, Sk, cw, koff, krow);
-    issue_tile<C>(Vh, vbuf0, 0, Sk, cw, voff, vrow);
-    if (ntiles > 1) issue_tile<C>(Kh, kbuf1, BC, Sk, cw, koff, krow);
+    copy_tile<C, false>(Kh, kbuf0, 0, Sk, cw, lane, cl);
+    if (ntiles > 1) copy_tile<C, false>(Kh, kbuf1, BC, Sk, cw, lane, cl);
   }
 
   // Q fragments (B operand of S^T = K * Q^T): lane holds Q[my_q][ch*16 + hh*8 .. +8].
@@ -152,103 +222,62 @@ __global__ __launch_bounds__(64 * WAVES, D <= 128 ? 2 : 1) void fa_fwd_bf16_kern
 #pragma unroll
   for (int d4 = 0; d4 < C::NVOFF; ++d4) v_off[d4] = v_row + (((4 * d4 + vx) ^ vsw) << 4);
 
+  // Row sums of the bf16 weights on the matrix cores: one 16x16x32 product per
+  // 16-key chunk with the weights' B operand as it stands and a 0/1 A operand
+  // that picks, for output rows 0-3 and 8-11, the chunk's keys of query n and,
+  // for rows 4-7 and 12-15, those of query n + 16.  Then every accumulator
+  // register of lane l holds the sum for query l % 32 (both lane halves).
+  bf16x8 sel;
+  {
+    const __bf16 one = (__bf16)((((lane & 15) >> 2) & 1) == ((lane >> 4) & 1) ? 1.0f : 0.0f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sel[e] = one;
+  }
+
   f32x16 acc[C::DB];
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
+  f32x4 l_mfma = f32x4{};   // sum of bf16(p) on the matrix cores (MFMA_SUM)
+  float l_round = 0.0f;     // this lane's share of sum(bf16(p)) (otherwise)
   float m_run = -INFINITY;  // reference max of the raw (unscaled) scores
   float l_exact = 0.0f;     // this lane's share of sum(p) with float32 weights
-  float l_round = 0.0f;     // this lane's share of sum(bf16(p)), the weights P*V used
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  bf16x8 pf[C::PCH];        // bf16 weights of the tile whose P*V is pending
 
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  // S tiles in two named buffers used alternately (no copy between tiles).
-  f32x16 s_a[C::KB], s_b[C::KB];
-  float mt_a = 0.0f, mt_b = 0.0f;  // row max of s_a / s_b
-  if (wave_ntiles > 0) {
-    qk_tile<C>(s_a, kbuf0, qf, k_off);
-    mt_a = row_max<C>(s_a, hh);
-  }
-  __syncthreads();  // every wave is done with K(0) before K(2) overwrites it
-
-  // Iteration j: start K(j+2) and V(j+1); compute S(j+1) into s_out while the
-  // weights of tile j (s_in) form; then O += P(j) V(j).
-  auto step = [&](const int j, lds_u8* k_next, lds_u8* k_load, const lds_u8* v_cur,
-                  lds_u8* v_load, f32x16 (&s_in)[C::KB], f32x16 (&s_out)[C::KB],
-                  float& mt_in, float& mt_out) {
-    if (copier) {
-      if (j + 2 < ntiles) issue_tile<C>(Kh, k_load, (j + 2) * BC, Sk, cw, koff, krow);
-      if (j + 1 < ntiles) issue_tile<C>(Vh, v_load, (j + 1) * BC, Sk, cw, voff, vrow);
+  const auto needs_mask = [&](int k0) {
+    return (CAUSAL && (k0 + BC - 1 > qw0 + kshift)) || (k0 + BC > Sk);
+  };
+  const auto apply_mask = [&](f32x16 (&s)[C::KB], int k0) {
+    const int lim = (CAUSAL ? min(my_q + kshift, Sk - 1) : (Sk - 1)) - k0 - hh * 8;
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kb * 32 + (r >> 3) * 16 + (r & 7);
+        s[kb][r] = key > lim ? -INFINITY : s[kb][r];
+      }
+  };
+  // Weights of 16-key chunk pc of a tile (this lane's 8 keys): bf16 B operand.
+  const auto weights = [&](const f32x16 (&s)[C::KB], int pc, float mc, float& rs) {
+    bf16x8 w;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float p = fast_exp2(fmaf(s[pc >> 1][(pc & 1) * 8 + e], c, -mc));
+      rs += p;
+      w[e] = (__bf16)p;
     }
-    if (j < wave_ntiles) {
-      const int k0 = j * BC;
-      // ---- mask (diagonal and tail tiles only) and the tile's row max -------
-      // (for unmasked tiles the max was taken during the previous tile)
-      float mt = mt_in;
-      if ((CAUSAL && (k0 + BC - 1 > qw0 + kshift)) || (k0 + BC > Sk)) {
-        const int lim = (CAUSAL ? min(my_q + kshift, Sk - 1) : (Sk - 1)) - k0 - hh * 8;
-#pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kb * 32 + (r >> 3) * 16 + (r & 7);
-            s_in[kb][r] = key > lim ? -INFINITY : s_in[kb][r];
-          }
-        mt = row_max<C>(s_in, hh);
-      }
-      // ---- the (rare) move of the reference max ------------------------------
-      // true on the first tile with a visible key for some row (m_run = -inf
-      // there); for a row with no visible key yet, -inf - -inf is NaN and the
-      // comparison is false
-      if (__any((mt - m_run) * c > kRescaleThreshold)) {
-        const float m_new = fmaxf(m_run, mt);
-        // 0 when the row's first keys arrive; 1 for rows whose reference
-        // does not move (also rows that have seen no key yet: -inf, -inf)
-        const float alpha = m_new == m_run ? 1.0f : fast_exp2((m_run - m_new) * c);
-        m_run = m_new;
-        l_exact *= alpha;
-        l_round *= alpha;
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) acc[db] *= alpha;
-      }
-      // A row whose reference is still -inf has only masked keys in this tile
-      // (a finite one would have moved the reference above): its weights are
-      // exp2(-inf - 0) = 0.
-      const float mc = m_run == -INFINITY ? 0.0f : m_run * c;
-
-      // ---- S(j+1) on the matrix cores (result unused past the last tile) ---
-      qk_tile<C>(s_out, k_next, qf, k_off);
-
-      // ---- weights of tile j: p = 2^(s*c - m*c), rounded to bf16 -------------
-      float rs = 0.0f;
-      bf16x8 pf[C::PCH];
-#pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(fmaf(s_in[kb][r], c, -mc));
-          rs += p;
-          pf[2 * kb + (r >> 3)][r & 7] = (__bf16)p;
-        }
-
-      // ---- O^T += V^T * P^T -------------------------------------------------
-      // Key-chunk-major: the chunks of the first 32 keys only need the first
-      // half of the weights, so the second half's exponentials overlap them.
+    return w;
+  };
+  // A row that has seen no key keeps m_run = -inf; its weights are
+  // exp2(-inf - 0) = 0.
+  const auto ref_mc = [&]() { return m_run == -INFINITY ? 0.0f : m_run * c; };
+  // Sums of the bf16 weights of a tile (before its P*V, i.e. after its check).
+  const auto weight_sums = [&]() {
+    if constexpr (MFMA_SUM) {
 #pragma unroll
       for (int pc = 0; pc < C::PCH; ++pc)
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-          const lds_u8* p = v_cur + pc * 16 * C::ROW_BYTES + (db / C::NVOFF) * 256 +
-                            v_off[db % C::NVOFF];
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
-          const s16x4 hi =
-              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * C::ROW_BYTES));
-          const bf16x8 vf = __builtin_bit_cast(
-              bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[pc], acc[db], 0, 0, 0);
-        }
-      // ---- running sums: float32 weights and the bf16 weights P*V used ------
-      l_exact += rs;
+        l_mfma = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, pf[pc], l_mfma, 0, 0, 0);
+    } else {
 #pragma unroll
       for (int pc = 0; pc < C::PCH; ++pc)
 #pragma unroll
@@ -256,39 +285,152 @@ __global__ __launch_bounds__(64 * WAVES, D <= 128 ? 2 : 1) void fa_fwd_bf16_kern
           const bf16x2 two = {pf[pc][2 * t], pf[pc][2 * t + 1]};
           l_round = __builtin_amdgcn_fdot2_f32_bf16(two, ones, l_round, false);
         }
-      // ---- row max of S(j+1) for the next tile ------------------------------
-      mt_out = row_max<C>(s_out, hh);
+    }
+  };
+  const auto pv_chunk = [&](const lds_u8* v_cur, int pc) {
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      const lds_u8* p = v_cur + pc * 16 * C::ROW_BYTES + (db / C::NVOFF) * 256 +
+                        v_off[db % C::NVOFF];
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+      const s16x4 hi =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * C::ROW_BYTES));
+      const bf16x8 vf =
+          __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[pc], acc[db], 0, 0, 0);
+    }
+  };
+  // The rare path: some weight of tile s (masked, with the reference mc) was
+  // above the limit.  Raise the reference to the row max seen so far, rescale
+  // what was accumulated (tiles up to the previous one), and form the tile's
+  // weights again.
+  const auto raise_reference = [&](const f32x16 (&s)[C::KB], float& rs) {
+    // (The weights formed before are replaced; this use keeps their
+    // computation where the instruction order put it.)
+#pragma unroll
+    for (int pc = 0; pc < C::PCH; ++pc) asm volatile("" ::"v"(pf[pc]));
+    const float mt = row_max<C>(s, hh);
+    const float m_new = fmaxf(m_run, mt);
+    const float alpha = m_new == m_run ? 1.0f : fast_exp2((m_run - m_new) * c);
+    m_run = m_new;
+    l_exact *= alpha;
+    l_round *= alpha;
+    l_mfma *= alpha;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) acc[db] *= alpha;
+    const float mc = ref_mc();
+    rs = 0.0f;
+#pragma unroll
+    for (int pc = 0; pc < C::PCH; ++pc) pf[pc] = weights(s, pc, mc, rs);
+  };
 
-      // Instruction order for the region: every MFMA (S(j+1), then P*V) is
-      // followed by its share of the VALU work (exponentials, conversions, row
-      // sums, the next tile's row max) and its operand reads, which run kLead
-      // MFMAs ahead of their use.
-      constexpr int kLead = 3;
-      __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);  // LDS read (K)
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  // S tiles in two named buffers used alternately (no copy between tiles).
+  f32x16 s_a[C::KB], s_b[C::KB];
+  if (wave_ntiles > 0) {
+    // S(0) and the reference max from it: every row that sees any key sees
+    // key 0, so only rows that see nothing keep -inf.
+    qk_tile<C>(s_a, kbuf0, qf, k_off);
+    if (needs_mask(0)) apply_mask(s_a, 0);
+    m_run = row_max<C>(s_a, hh);
+  }
+  __syncthreads();  // every wave is done with K(0) before K(2) overwrites it
+
+  // Step t: reads K(t+1) from k_next and V(t-1) from v_prev; copies K(t+2)
+  // into k_load (K(t)'s buffer) and V(t) into v_load (V(t-2)'s buffer).
+  // S(t) is in s_in; S(t+1) goes to s_out.  Three kinds of step:
+  //  kFirst (t = 0):    weights of tile 0, S(1) if the wave needs tile 1;
+  //  kFull  (1 <= t, t + 1 < wave_ntiles): P*V of t-1, weights of t, S(t+1),
+  //                     under a fixed instruction order;
+  //  kTail  (the wave's last steps): P*V of t-1 if the wave has it, weights
+  //                     of t if the wave has tile t, no S.
+  // Every path gives the weights and S buffers defined values, so that their
+  // previous contents are not kept alive across a step.
+  constexpr int kFirst = 0, kFull = 1, kTail = 2;
+  auto step = [&](auto kind_tag, const int t, const lds_u8* k_next, lds_u8* k_load,
+                  const lds_u8* v_prev, lds_u8* v_load, f32x16 (&s_in)[C::KB],
+                  f32x16 (&s_out)[C::KB]) {
+    constexpr int KIND = decltype(kind_tag)::value;
+    if (copier) {
+      if (t + 2 < ntiles) copy_tile<C, false>(Kh, k_load, (t + 2) * BC, Sk, cw, lane, cl);
+      if (t < ntiles) copy_tile<C, true>(Vh, v_load, t * BC, Sk, cw, lane, cl);
+    }
+    const bool do_sm = KIND == kFull || t < wave_ntiles;
+    if (KIND != kFirst && do_sm && needs_mask(t * BC)) apply_mask(s_in, t * BC);
+    const float mc = ref_mc();
+    float rs = 0.0f;
+    if constexpr (KIND == kFull) {
+      weight_sums();
 #pragma unroll
-      for (int i = 0; i < C::KB * C::KCH; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-        __builtin_amdgcn_sched_group_barrier(0x002, C::VALU_PER_MFMA, 0);  // VALU
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kLead, 0);  // LDS read (V)
+      for (int pc = 0; pc < C::PCH; ++pc) pv_chunk(v_prev, pc);
 #pragma unroll
-      for (int i = 0; i < C::DB * C::PCH; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS read
-        __builtin_amdgcn_sched_group_barrier(0x002, C::VALU_PER_MFMA, 0);  // VALU
+      for (int pc = 0; pc < C::PCH; ++pc) pf[pc] = weights(s_in, pc, mc, rs);
+      qk_tile<C>(s_out, k_next, qf, k_off);
+      // Instruction order: the bf16-weight sums, then P(t-1)*V(t-1) chunk by
+      // chunk (two transposing reads per product), then S(t+1) (one read per
+      // product); operand reads run three products ahead; the vector work of
+      // tile t is spread evenly over the products.
+      step_schedule<C, MFMA_SUM>(std::make_integer_sequence<int, (MFMA_SUM ? C::PCH : 0) +
+                                                                 C::DB * C::PCH + C::KB * C::KCH>{});
+    } else {
+      if (KIND == kTail && t - 1 < wave_ntiles) {
+        weight_sums();
+#pragma unroll
+        for (int pc = 0; pc < C::PCH; ++pc) pv_chunk(v_prev, pc);
       }
+      if (do_sm) {
+#pragma unroll
+        for (int pc = 0; pc < C::PCH; ++pc) pf[pc] = weights(s_in, pc, mc, rs);
+      } else {
+#pragma unroll
+        for (int pc = 0; pc < C::PCH; ++pc) pf[pc] = bf16x8{};
+      }
+      if (KIND == kFirst && t + 1 < wave_ntiles) {
+        qk_tile<C>(s_out, k_next, qf, k_off);
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb) s_out[kb] = f32x16{};
+      }
+    }
+    if (do_sm) {
+      // The reference moves only if some weight of this tile is too large
+      // (or not finite); for a row that sees no key all weights are 0.
+      if (__any(!(rs <= kRowSumLimit))) raise_reference(s_in, rs);
+      l_exact += rs;
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
-  for (int j = 0; j < ntiles; j += 2) {
-    step(j, kbuf1, kbuf0, vbuf0, vbuf1, s_a, s_b, mt_a, mt_b);
-    if (j + 1 < ntiles) step(j + 1, kbuf0, kbuf1, vbuf1, vbuf0, s_b, s_a, mt_b, mt_a);
+  const std::integral_constant<int, kFirst> first{};
+  const std::integral_constant<int, kFull> full{};
+  const std::integral_constant<int, kTail> tail{};
+  // Steps 0 .. ntiles (the last one only finishes P*V of the last tile).  The
+  // full steps run in pairs so that buffer and S parity are static; the tail
+  // steps of the wave follow.  Every wave takes ntiles + 1 steps (barriers).
+  step(first, 0, kbuf1, kbuf0, vbuf1, vbuf0, s_a, s_b);
+  int t = 1;
+  const int t_tail = max(1, wave_ntiles - 1);  // first tail step
+  for (; t + 1 < t_tail; t += 2) {
+    step(full, t, kbuf0, kbuf1, vbuf0, vbuf1, s_b, s_a);
+    step(full, t + 1, kbuf1, kbuf0, vbuf1, vbuf0, s_a, s_b);
   }
+  if (t < t_tail) {
+    step(full, t, kbuf0, kbuf1, vbuf0, vbuf1, s_b, s_a);
+    ++t;
+  }
+  if (!(t & 1) && t <= ntiles) {
+    step(tail, t, kbuf1, kbuf0, vbuf1, vbuf0, s_a, s_b);
+    ++t;
+  }
+  for (; t + 1 <= ntiles; t += 2) {
+    step(tail, t, kbuf0, kbuf1, vbuf0, vbuf1, s_b, s_a);
+    step(tail, t + 1, kbuf1, kbuf0, vbuf1, vbuf0, s_a, s_b);
+  }
+  if (t <= ntiles) step(tail, t, kbuf0, kbuf1, vbuf0, vbuf1, s_b, s_a);
 
-  const float lr = l_round + swap_halves(l_round, hh);
   const float le = l_exact + swap_halves(l_exact, hh);
+  const float lr = MFMA_SUM ? l_mfma[0] : l_round + swap_halves(l_round, hh);
   if (my_q >= Sq) return;
   // O is normalised by the sum of the bf16 weights that multiplied V, so the
   // weights applied to V sum to one exactly (up to float32 rounding); the
@@ -302,11 +444,11 @@ __global__ __launch_bounds__(64 * WAVES, D <= 128 ? 2 : 1) void fa_fwd_bf16_kern
       // registers gq*4 .. gq*4+3 hold head-dim entries db*32 + gq*8 + hh*4 + 0..3
       u32x2 pk;
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const __bf16 lo = (__bf16)(acc[db][gq * 4 + 2 * t] * inv);
-        const __bf16 hi = (__bf16)(acc[db][gq * 4 + 2 * t + 1] * inv);
-        pk[t] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
-                ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+      for (int tt = 0; tt < 2; ++tt) {
+        const __bf16 lo = (__bf16)(acc[db][gq * 4 + 2 * tt] * inv);
+        const __bf16 hi = (__bf16)(acc[db][gq * 4 + 2 * tt + 1] * inv);
+        pk[tt] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+                 ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
       }
       *reinterpret_cast<u32x2*>(Orow + db * 32 + gq * 8 + hh * 4) = pk;
     }
@@ -887,10 +1029,10 @@ int run_bf16(const void* q, const void* k, const void* v, void* o, float* lse, i
                   V, Out, lse, Sq, Sk, cfg.nq, p.bh_total, p.group_heads, p.c);
   } else {
     if (causal)
-      return launch(fa_fwd_bf16_kernel<D, BC, WAVES, true>, cfg.grid, 64 * WAVES, stream, Q, K, V,
-                    Out, lse, Sq, Sk, cfg.nq, p.bh_total, p.group_heads, p.c);
-    return launch(fa_fwd_bf16_kernel<D, BC, WAVES, false>, cfg.grid, 64 * WAVES, stream, Q, K, V,
-                  Out, lse, Sq, Sk, cfg.nq, p.bh_total, p.group_heads, p.c);
+      return launch(fa_fwd_bf16_kernel<D, BC, WAVES, true, kMfmaSum>, cfg.grid, 64 * WAVES, stream,
+                    Q, K, V, Out, lse, Sq, Sk, cfg.nq, p.bh_total, p.group_heads, p.c);
+    return launch(fa_fwd_bf16_kernel<D, BC, WAVES, false, kMfmaSum>, cfg.grid, 64 * WAVES, stream,
+                  Q, K, V, Out, lse, Sq, Sk, cfg.nq, p.bh_total, p.group_heads, p.c);
   }
 }
 
