@@ -238,9 +238,12 @@ __device__ __forceinline__ CopyLanes copy_lanes(int part, int lane) {
   // share's first row is a multiple of P lines, a lane's row within piece 0
   // adds < 4 lines, and piece u adds 4u lines with 4u + 3 < P.
   constexpr int P = C::CH_PER_LINE / C::ROWS_PER_LINE;
-  static_assert(C::ROW_BYTES <= 256 && C::ROWS_PER_LOAD == 4 * C::ROWS_PER_LINE &&
-                    (C::LOADS_PER_WAVE * C::ROWS_PER_LOAD / C::ROWS_PER_LINE) % P == 0 &&
-                    4 * C::LOADS_PER_WAVE <= P,
+  // (With one piece per wave nothing is assumed about later pieces.)
+  static_assert(C::ROW_BYTES <= 256 &&
+                    (C::LOADS_PER_WAVE == 1 ||
+                     (C::ROWS_PER_LOAD == 4 * C::ROWS_PER_LINE &&
+                      (C::LOADS_PER_WAVE * C::ROWS_PER_LOAD / C::ROWS_PER_LINE) % P == 0 &&
+                      4 * C::LOADS_PER_WAVE <= P)),
                 "piece u's K swizzle must be piece 0's XOR 4u");
   const int row0 = part * C::LOADS_PER_WAVE * C::ROWS_PER_LOAD + lane / C::RC;
   CopyLanes cl;

@@ -78,12 +78,9 @@ __device__ __forceinline__ void sched_group() {
 // followed by the operand reads of the product kLead places later (two
 // transposing V reads for a P*V product, one K read for an S product) and by
 // its share of the step's exponentials and other vector instructions.
-#ifndef FA_READ_LEAD
-#define FA_READ_LEAD 3
-#endif
 template <class C, bool MFMA_SUM, int N>
 struct StepOrder {
-  static constexpr int kLead = FA_READ_LEAD;
+  static constexpr int kLead = 3;
   static constexpr int kSum = MFMA_SUM ? C::PCH : 0;
   static constexpr int kPV = C::DB * C::PCH;
   // one exponential per score; an FMA and an add per score, a bf16 pack per
@@ -91,20 +88,17 @@ struct StepOrder {
   // matrix cores
   static constexpr int kTrans = C::KB * 16;
   static constexpr int kValu = C::KB * 16 * 2 + C::KB * 8 + (MFMA_SUM ? 0 : C::PCH * 4);
-  // operand reads issued after product i: those of product i + kLead
-  static constexpr int reads(int i) {
-    const int j = i + kLead - kSum;  // index among the P*V and S products
-    if (j < 0) return 0;
-    if (j < kPV) return 2;
-    return j < N - kSum ? 1 : 0;
-  }
+  // operand reads issued after product i: those of product i + kLead (the
+  // bf16-weight sums read no operands)
+  static constexpr int reads_of(int j) { return j < 0 ? 0 : j < kPV ? 2 : j < N - kSum ? 1 : 0; }
+  static constexpr int reads(int i) { return reads_of(i + kLead - kSum); }
   // reads of the products that start before any product has issued
   static constexpr int first_reads() {
     int n = 0;
-    for (int j = 0; j < kLead - kSum && j < N - kSum; ++j) n += j < kPV ? 2 : 1;
+    for (int j = 0; j < kLead - kSum; ++j) n += reads_of(j);
     return n;
   }
-  // product i's share of `total` instructions, spread evenly
+  // product i's share of `total` instructions, spread evenly over the products
   static constexpr int share(int i, int total) { return ((i + 1) * total) / N - (i * total) / N; }
 };
 
@@ -182,10 +176,11 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fa_fwd_bf16_kernel(
   const int wave_klast = CAUSAL ? min(qw0 + kRowsPerWave - 1 + kshift, Sk - 1) : (Sk - 1);
   const int wave_ntiles = (qw0 < Sq && wave_klast >= 0) ? min(ntiles, wave_klast / BC + 1) : 0;
 
-  // Copy waves: the last COPY_WAVES waves (all of a 4-wave workgroup; waves
-  // 4..7, one per SIMD, of an 8-wave one).
-  const bool copier = wave >= WAVES - C::COPY_WAVES;
-  const int cw = copier ? wave - (WAVES - C::COPY_WAVES) : 0;  // this wave's share of each copy
+  // Copy waves: the first COPY_WAVES waves (all of a 4-wave workgroup; waves
+  // 0..3, one per SIMD, of an 8-wave one).  Those are the older wave of each
+  // SIMD pair, which the matrix core serves first.
+  const bool copier = wave < C::COPY_WAVES;
+  const int cw = copier ? wave : 0;  // this wave's share of each copy
   const CopyLanes cl = copy_lanes<C>(cw, lane);
 
   // K(0) and K(1) now; step t copies K(t+2) and V(t).
@@ -260,11 +255,18 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fa_fwd_bf16_kernel(
   // Weights of 16-key chunk pc of a tile (this lane's 8 keys): bf16 B operand.
   const auto weights = [&](const f32x16 (&s)[C::KB], int pc, float mc, float& rs) {
     bf16x8 w;
+    // two scores at a time, so that no exponential is followed at once by
+    // its use
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float p = fast_exp2(fmaf(s[pc >> 1][(pc & 1) * 8 + e], c, -mc));
-      rs += p;
-      w[e] = (__bf16)p;
+    for (int e = 0; e < 8; e += 2) {
+      const float x0 = fmaf(s[pc >> 1][(pc & 1) * 8 + e], c, -mc);
+      const float x1 = fmaf(s[pc >> 1][(pc & 1) * 8 + e + 1], c, -mc);
+      const float p0 = fast_exp2(x0);
+      const float p1 = fast_exp2(x1);
+      rs += p0;
+      rs += p1;
+      w[e] = (__bf16)p0;
+      w[e + 1] = (__bf16)p1;
     }
     return w;
   };
@@ -361,12 +363,40 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fa_fwd_bf16_kernel(
     const float mc = ref_mc();
     float rs = 0.0f;
     if constexpr (KIND == kFull) {
+      // Operand reads in the order they are issued: each pair of products
+      // has its second product's reads first, so that the wait for the first
+      // product's operands covers the second's as well.
+      bf16x8 vf[C::PCH * C::DB], kf[C::KB * C::KCH];
+#pragma unroll
+      for (int f = 0; f < C::PCH * C::DB; ++f) {
+        const int g = f ^ 1;
+        const lds_u8* p = v_prev + (g / C::DB) * 16 * C::ROW_BYTES +
+                          ((g % C::DB) / C::NVOFF) * 256 + v_off[(g % C::DB) % C::NVOFF];
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+        const s16x4 hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * C::ROW_BYTES));
+        vf[g] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+#pragma unroll
+      for (int f = 0; f < C::KB * C::KCH; ++f) {
+        const int g = f ^ 1;
+        const int kb = g / C::KCH, ch = g % C::KCH;
+        kf[g] = *(const lds_bf16x8*)(k_next + kb * 32 * C::ROW_BYTES + (ch / C::NKOFF) * 256 +
+                                      k_off[ch % C::NKOFF]);
+      }
       weight_sums();
 #pragma unroll
-      for (int pc = 0; pc < C::PCH; ++pc) pv_chunk(v_prev, pc);
+      for (int f = 0; f < C::PCH * C::DB; ++f)
+        acc[f % C::DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[f], pf[f / C::DB],
+                                                                 acc[f % C::DB], 0, 0, 0);
 #pragma unroll
       for (int pc = 0; pc < C::PCH; ++pc) pf[pc] = weights(s_in, pc, mc, rs);
-      qk_tile<C>(s_out, k_next, qf, k_off);
+#pragma unroll
+      for (int f = 0; f < C::KB * C::KCH; ++f) {
+        const int kb = f / C::KCH, ch = f % C::KCH;
+        s_out[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[f], qf[ch],
+                                                            ch == 0 ? f32x16{} : s_out[kb], 0, 0, 0);
+      }
       // Instruction order: the bf16-weight sums, then P(t-1)*V(t-1) chunk by
       // chunk (two transposing reads per product), then S(t+1) (one read per
       // product); operand reads run three products ahead; the vector work of
