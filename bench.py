@@ -5,8 +5,12 @@ One step = one call of fa_fwd over the whole workload (inputs resident in HBM
 before timing starts).  Default workload: causal bf16 attention, B=1 H=32
 S=16384 D=128 (the long-sequence causal shape with S >= 4096 and D = 128).
 Prints ONE JSON line on stdout; a per-workload table goes to stderr with
---all.  The line's "secondary" object adds, outside `value`, the queries-
-against-a-prefix path (prefill, decode), the merge and the backward pass.
+--all.  The line's "secondary" object adds, outside `value`, the forward on
+the other workloads (S = 4096 D = 128 causal and unmasked, S = 8192 D = 256,
+S = 1024 D = 64), the queries-against-a-prefix path (prefill, decode), the
+merge and the backward pass.  The secondary work runs first, so the headline
+launches start on a GPU whose shader clock has settled under load (the
+timed region is still exactly --steps launches after --warmup untimed ones).
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                   [--all] [--no-cpu-baseline] [--copy-calibration]
@@ -74,12 +78,14 @@ def recorded_traffic(workload: str):
     return recorded_profile_value(workload, "traffic_bytes_per_launch")
 
 
-def time_workload(w, causal, steps, warmup, cold_launches=0):
+def time_workload(w, causal, steps, warmup, cold_launches=0, inputs=None):
+    """Time `steps` back-to-back launches after `warmup` untimed ones; inputs
+    (q, k, v on the GPU) are made here unless given."""
     import torch
     import exact_attention_67_amd as fa
     from tests import workloads as wl
 
-    q, k, v = wl.make_inputs(w, device="cuda")
+    q, k, v = wl.make_inputs(w, device="cuda") if inputs is None else inputs
     out = torch.empty_like(q)
     lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
@@ -159,14 +165,63 @@ def _time_launches(fn, steps, warmup):
     return sum(per) / len(per), per[len(per) // 2], per[0]
 
 
+def kernel_name(w, causal) -> str:
+    """Name of the forward kernel fa_fwd launches for workload w (from the
+    host-side launch plan)."""
+    import torch
+    import exact_attention_67_amd as fa
+    c = "true" if causal else "false"
+    if w.dtype != torch.bfloat16:
+        return f"fa_fwd_f32_kernel<{w.D},{c}>"
+    plan = fa.fa_fwd_plan(w.B, w.H, w.S, w.D, int(causal), 2)
+    waves, bc = plan["threads"] // 64, plan["keys_per_tile"]
+    if w.D == 256:
+        return f"fa_fwd_bf16_ring_kernel<{w.D},{bc},{waves},{c}>"
+    return f"fa_fwd_bf16_kernel<{w.D},{bc},{waves},{c},true>"
+
+
+# forward figures beside the headline: (workload, causal)
+SECONDARY_FWD = (("c3_bf16_2x16x4096x128", True), ("c3_bf16_2x16x4096x128", False),
+                 ("c5_bf16_causal_2x8x8192x256_stress", True),
+                 ("c2_bf16_causal_4x16x1024x64", True))
+
+
+def time_secondary_forward():
+    """The forward on the other workloads: warm-up launches worth about 200 ms
+    of GPU time, then back-to-back launches worth about 50 ms, timed as the
+    headline (TFLOP/s over the whole timed region)."""
+    import torch
+    from tests import workloads as wl
+    out = {}
+    for name, causal in SECONDARY_FWD:
+        w = wl.WORKLOADS[name]
+        probe = time_workload(w, causal, 3, 1)
+        warm = max(3, min(2000, int(200.0 / max(probe["ms_per_step"], 1e-3))))
+        steps = max(10, min(500, int(50.0 / max(probe["ms_per_step"], 1e-3))))
+        r = time_workload(w, causal, steps, warm)
+        tf = w.flops(causal) / (r["ms_per_step"] * 1e-3) / 1e12
+        key = f"forward_{name}_{'causal' if causal else 'full'}"
+        out[key] = {"tflops": round(tf, 2), "pct_of_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+                    "ms_per_step": round(r["ms_per_step"], 5), "steps": steps, "warmup": warm,
+                    "launch_ms_avg": round(r["launch_ms_avg"], 5),
+                    "launch_ms_median": round(r["launch_ms_med"], 5),
+                    "causal": causal, "flops_per_launch": w.flops(causal),
+                    "kernel": kernel_name(w, causal)}
+        log(f"[bench] {key}: {r['ms_per_step']:.4f} ms/step, {tf:.1f} TFLOP/s "
+            f"({100 * tf / PEAK_BF16_TFLOPS:.1f}% of peak)")
+        torch.cuda.empty_cache()
+    return out
+
+
 def time_secondary(steps):
-    """The Sq != Sk path (chunked prefill, decode) and the merge over key sets,
-    each on its own synthetic workload; reported beside the headline figure."""
+    """The other forward workloads, the Sq != Sk path (chunked prefill,
+    decode), the merge over key sets and the backward pass, each on its own
+    synthetic workload; reported beside the headline figure."""
     import torch
     import exact_attention_67_amd as fa
     from tests import workloads as wl
 
-    out = {}
+    out = time_secondary_forward()
     for name, w in wl.PREFIX_WORKLOADS.items():
         q, k, v = (t.cuda() for t in wl.make_prefix_inputs(w))
         o = torch.empty_like(q)
@@ -230,13 +285,15 @@ def time_secondary(steps):
 def cpu_baseline(w, causal, budget_s=20.0):
     """The oracle, as it stands, on the host cores over a bounded sample of the
     same workload: whole heads (row-blocked), one after another until the time
-    budget is spent (or every head is done)."""
+    budget is spent (or every head is done).  Torch runs one thread per host
+    CPU this process may run on (all of them unless the process is pinned)."""
     import torch
     from oracle import attention as orc
     from tests import workloads as wl
 
-    threads = max(1, min(16, os.cpu_count() or 1))
-    torch.set_num_threads(threads)
+    cores = os.cpu_count() or 1
+    usable = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else cores
+    torch.set_num_threads(max(1, usable))
     q, k, v = wl.make_inputs(w)
     flops_head = 4.0 * w.S * w.S * w.D * (0.5 if causal else 1.0)
     heads = [(b, h) for b in range(w.B) for h in range(w.H)]
@@ -252,7 +309,9 @@ def cpu_baseline(w, causal, budget_s=20.0):
     return {
         "value": flops_head * done / t_total / 1e12,
         "unit": "TFLOP/s",
-        "cores": torch.get_num_threads(),
+        "cores": cores,
+        "cores_usable": usable,
+        "threads": torch.get_num_threads(),
         "kind": "oracle",
         "sample": f"{done} of {len(heads)} heads of {w.name} "
                   f"({'causal' if causal else 'non-causal'}), float64 torch CPU, "
@@ -312,9 +371,15 @@ def main():
 
     w = wl.WORKLOADS[a.workload]
     causal = (not a.noncausal) and (True in w.causal)
+    # The headline inputs are made (on the host, then copied) before the
+    # secondary figures, so that the headline launches follow those without
+    # an idle gap (see the module docstring).
+    inputs = wl.make_inputs(w, device="cuda")
+    secondary = None if a.no_secondary else time_secondary(max(5, a.steps // 5))
+
     log(f"[bench] {w.name} causal={causal} steps={a.steps} warmup={a.warmup}")
     r = time_workload(w, causal, a.steps, a.warmup,
-                      cold_launches=0 if a.no_cold else min(20, a.steps))
+                      cold_launches=0 if a.no_cold else min(20, a.steps), inputs=inputs)
     flops = w.flops(causal)
     value = flops / (r["ms_per_step"] * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == torch.bfloat16 else PEAK_F32_TFLOPS
@@ -352,13 +417,12 @@ def main():
                 log(f"{name:40s} {'causal' if c else 'full':7s} {rr['ms_per_step']:9.4f} "
                     f"{tf:9.1f} {100 * tf / pk:6.1f} {rr['launch_ms_avg']:15.4f}")
 
-    secondary = None if a.no_secondary else time_secondary(max(5, a.steps // 5))
-
     cpu = None
     if rank == 0 and not a.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample ...")
         cpu = cpu_baseline(w, causal, a.cpu_budget)
-        log(f"[bench] cpu oracle: {cpu['value'] * 1e3:.1f} GFLOP/s on {cpu['cores']} threads")
+        log(f"[bench] cpu oracle: {cpu['value'] * 1e3:.1f} GFLOP/s on {cpu['threads']} threads "
+            f"({cpu['cores']} host CPUs)")
 
     line = {
         "metric": METRIC,
@@ -383,7 +447,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
             "traffic": recorded_traffic(w.name),
-            "kernel": "fa_fwd_bf16_kernel" if w.dtype == torch.bfloat16 else "fa_fwd_f32_kernel",
+            "kernel": kernel_name(w, causal),
             "launch_ms_avg": round(r["launch_ms_avg"], 5),
             "launch_ms_median": round(r["launch_ms_med"], 5),
             "launch_ms_min": round(r["launch_ms_min"], 5),
@@ -396,8 +460,8 @@ def main():
         },
         "cold": cold,
         "cpu_baseline": cpu,
-        # not part of `value`: the Sq != Sk path, the merge and the backward pass,
-        # each on its own workloads
+        # not part of `value`: the forward on the other workloads, the Sq != Sk
+        # path, the merge and the backward pass, each on its own workloads
         "secondary": secondary,
     }
     if rank == 0:

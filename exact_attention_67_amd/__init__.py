@@ -51,6 +51,14 @@ def _stream(stream, device):
     return stream if stream is not None else torch.cuda.current_stream(device)
 
 
+def _on_device(what: str, tensors, device) -> None:
+    """Every tensor must live on `device` (a GPU): the kernels read and write
+    them through plain device pointers."""
+    for t in tensors:
+        if not t.is_cuda or t.device != device:
+            raise ValueError(f"{what} must be GPU tensors on {device} (got {t.device})")
+
+
 def forward(q, k, v, causal: bool = True, scale: Optional[float] = None,
             out=None, lse=None, stream=None) -> Tuple[object, object]:
     """Attention forward on torch tensors; returns (O, LSE).
@@ -62,8 +70,9 @@ def forward(q, k, v, causal: bool = True, scale: Optional[float] = None,
     """
     import torch
 
-    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+    if not q.is_cuda:
         raise ValueError("q, k, v must be GPU tensors")
+    _on_device("q, k, v", (k, v), q.device)
     if q.dtype != k.dtype or q.dtype != v.dtype:
         raise ValueError("q, k, v must share one dtype")
     if q.dtype not in (torch.bfloat16, torch.float32):
@@ -81,6 +90,7 @@ def forward(q, k, v, causal: bool = True, scale: Optional[float] = None,
             out = torch.empty_like(q)
         if lse is None:
             lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    _on_device("out and lse", (out, lse), q.device)
     if out.dtype != q.dtype or tuple(out.shape) != (B, H, S, D) or not out.is_contiguous():
         raise ValueError("out must be a contiguous [B,H,S,D] tensor of the input dtype")
     if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, S) or not lse.is_contiguous():
@@ -100,8 +110,9 @@ def forward_kv(q, k, v, causal: bool = True, scale: Optional[float] = None,
     visible key give O = 0, LSE = -inf).  Returns (O [B,H,Sq,D], LSE [B,H,Sq])."""
     import torch
 
-    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+    if not q.is_cuda:
         raise ValueError("q, k, v must be GPU tensors")
+    _on_device("q, k, v", (k, v), q.device)
     if not (q.dtype == k.dtype == v.dtype == torch.bfloat16):
         raise ValueError("forward_kv takes bf16 q, k, v")
     if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape:
@@ -120,6 +131,7 @@ def forward_kv(q, k, v, causal: bool = True, scale: Optional[float] = None,
             out = torch.empty_like(q)
         if lse is None:
             lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    _on_device("out and lse", (out, lse), q.device)
     if out.dtype != q.dtype or tuple(out.shape) != (B, H, Sq, D) or not out.is_contiguous():
         raise ValueError("out must be a contiguous bf16 [B,H,Sq,D] tensor")
     if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Sq) or not lse.is_contiguous():
@@ -136,8 +148,9 @@ def merge(o_parts, lse_parts, out=None, lse=None, stream=None) -> Tuple[object, 
     lse_parts float32 [G,B,H,S] -> (O [B,H,S,D] bf16, LSE [B,H,S] float32)."""
     import torch
 
-    if not (o_parts.is_cuda and lse_parts.is_cuda):
+    if not o_parts.is_cuda:
         raise ValueError("o_parts and lse_parts must be GPU tensors")
+    _on_device("o_parts and lse_parts", (lse_parts,), o_parts.device)
     if o_parts.dtype != torch.bfloat16 or lse_parts.dtype != torch.float32:
         raise ValueError("o_parts must be bf16 and lse_parts float32")
     if o_parts.dim() != 5 or tuple(lse_parts.shape) != tuple(o_parts.shape[:4]):
@@ -151,6 +164,7 @@ def merge(o_parts, lse_parts, out=None, lse=None, stream=None) -> Tuple[object, 
             out = torch.empty((B, H, S, D), dtype=torch.bfloat16, device=o_parts.device)
         if lse is None:
             lse = torch.empty((B, H, S), dtype=torch.float32, device=o_parts.device)
+    _on_device("out and lse", (out, lse), o_parts.device)
     if out.dtype != torch.bfloat16 or tuple(out.shape) != (B, H, S, D) or not out.is_contiguous():
         raise ValueError("out must be a contiguous bf16 [B,H,S,D] tensor")
     if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, S) or not lse.is_contiguous():
@@ -173,8 +187,9 @@ def backward(q, k, v, o, lse, dout, causal: bool = True, scale: Optional[float] 
     import torch
 
     ts = (q, k, v, o, dout)
-    if not all(t.is_cuda for t in ts + (lse,)):
+    if not q.is_cuda:
         raise ValueError("inputs must be GPU tensors")
+    _on_device("inputs", ts + (lse,), q.device)
     if not all(t.dtype == torch.bfloat16 for t in ts) or lse.dtype != torch.float32:
         raise ValueError("q, k, v, o, dout must be bf16 and lse float32")
     if q.dim() != 4 or any(t.shape != q.shape for t in ts):

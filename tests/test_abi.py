@@ -1,6 +1,14 @@
 """Boundary tests that need no GPU: the library loads, exports every function
 include/fa.h declares, and rejects bad arguments on the host before any HIP
-call (so fake, never-dereferenced addresses are safe here)."""
+call.
+
+Shape, head-dimension, mask-flag and size-overflow rules are checked through
+the launch-shape queries, which make no HIP call at all.  The pointer rules
+(NULL, alignment, overlap) and the other rejections of the launching entry
+points are checked here with fake addresses only where no GPU is visible, so
+that a regression in the order of the checks can never launch a kernel on
+them; on a GPU the same rules are checked on real device buffers
+(test_validation_gpu.py)."""
 
 import math
 import os
@@ -45,8 +53,21 @@ def test_status_codes_match_header():
         assert getattr(_lib, name) == int(val), name
 
 
-# Fake, 256-byte-aligned, far-apart device addresses: never dereferenced
-# because every case below fails validation first.
+def _gpu_visible() -> bool:
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:  # pragma: no cover - torch is part of the image
+        return False
+
+
+# The fake-address tests run only where no kernel can be launched.
+no_device = pytest.mark.skipif(_gpu_visible(), reason=(
+    "passes fake device addresses to launching entry points; the GPU suite "
+    "checks the same rules on real buffers"))
+
+# Fake, 256-byte-aligned, far-apart device addresses (never dereferenced: on
+# a host without a GPU a launch could only fail).
 A = 1 << 40
 Q, K, V, O, L = (A * (i + 1) for i in range(5))
 
@@ -56,6 +77,7 @@ def call(q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, S=128, D=64, causal=1, scale=0.125
     return fn(q, k, v, o, lse, B, H, S, D, causal, scale, None)
 
 
+@no_device
 @pytest.mark.parametrize("f32", [False, True])
 def test_validation_errors(f32):
     assert call(q=0, f32=f32) == fa.FA_ERR_NULL
@@ -79,6 +101,7 @@ def test_validation_errors(f32):
     assert call(B=1 << 20, H=1 << 12, S=1024, D=64, f32=f32) == fa.FA_ERR_SHAPE
 
 
+@no_device
 @pytest.mark.parametrize("f32", [False, True])
 def test_alias_rejected(f32):
     es = 4 if f32 else 2
@@ -97,6 +120,7 @@ def call_kv(q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, Sq=64, Sk=300, D=128, causal=1,
     return fa.fa_fwd_kv(q, k, v, o, lse, B, H, Sq, Sk, D, causal, scale, None)
 
 
+@no_device
 def test_fwd_kv_validation_errors():
     for bad in ({"q": 0}, {"k": 0}, {"v": 0}, {"o": 0}, {"lse": 0}):
         assert call_kv(**bad) == fa.FA_ERR_NULL, bad
@@ -120,6 +144,7 @@ def call_merge(op=Q, lp=K, G=3, B=1, H=2, S=100, D=64, o=O, lse=L):
     return fa.fa_merge(op, lp, G, B, H, S, D, o, lse, None)
 
 
+@no_device
 def test_merge_validation_errors():
     for bad in ({"op": 0}, {"lp": 0}, {"o": 0}, {"lse": 0}):
         assert call_merge(**bad) == fa.FA_ERR_NULL, bad
@@ -145,6 +170,7 @@ def call_bwd(**kw):
                      b["scale"], None)
 
 
+@no_device
 def test_bwd_validation_errors():
     for name in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv", "delta"):
         assert call_bwd(**{name: 0}) == fa.FA_ERR_NULL, name
@@ -237,3 +263,41 @@ def test_plan_rejects_bad_shapes(args, status):
     with pytest.raises(fa.FAError) as e:
         fa.fa_fwd_plan(*args)
     assert e.value.status == status
+
+
+# The shape rules of fa_fwd / fa_fwd_f32 / fa_fwd_kv through the host-only
+# queries, which run the same checks as the launching entry points.
+@pytest.mark.parametrize("eb", [2, 4])
+def test_plan_shape_rules_of_fa_fwd(eb):
+    def status(B=1, H=2, S=128, D=64, causal=1):
+        try:
+            fa.fa_fwd_plan(B, H, S, D, causal, eb)
+            return fa.FA_OK
+        except fa.FAError as e:
+            return e.status
+    assert status() == fa.FA_OK
+    for bad in ({"B": 0}, {"H": 0}, {"S": 0}, {"B": -1}, {"S": -5}):
+        assert status(**bad) == fa.FA_ERR_SHAPE, bad
+    for d in (0, 1, 32, 96, 100, 192, 512):
+        assert status(D=d) == fa.FA_ERR_HEADDIM, d
+    for c in (-1, 2, 7):
+        assert status(causal=c) == fa.FA_ERR_CAUSAL, c
+    # overflow: S*D beyond 32-bit per head, grid beyond 2^31
+    assert status(S=1 << 24, D=256) == fa.FA_ERR_SHAPE
+    assert status(B=1 << 20, H=1 << 12, S=1024, D=64) == fa.FA_ERR_SHAPE
+
+
+def test_plan_shape_rules_of_fa_fwd_kv():
+    def status(B=1, H=2, Sq=64, Sk=300, D=128, causal=1):
+        try:
+            fa.fa_fwd_kv_plan(B, H, Sq, Sk, D, causal)
+            return fa.FA_OK
+        except fa.FAError as e:
+            return e.status
+    assert status() == fa.FA_OK
+    for bad in ({"Sq": 0}, {"Sk": 0}, {"Sq": -3}, {"Sk": -1}, {"B": 0}, {"H": -2}):
+        assert status(**bad) == fa.FA_ERR_SHAPE, bad
+    assert status(D=96) == fa.FA_ERR_HEADDIM
+    assert status(causal=2) == fa.FA_ERR_CAUSAL
+    assert status(Sk=1 << 24, D=256) == fa.FA_ERR_SHAPE
+    assert status(Sq=1 << 24, D=256) == fa.FA_ERR_SHAPE

@@ -1,0 +1,164 @@
+"""Argument checks of the launching entry points on real device buffers.
+
+Every pointer below is an offset into one zero-filled device allocation with
+room to spare, so even if a rejection stopped working the launch it let
+through would stay inside that allocation.  Each rejected call must leave the
+allocation untouched.  NULL pointers and size overflows are not passed here
+(a regression there could not be kept in bounds); test_abi.py checks those on
+a host without a GPU, and the shape rules through the host-only launch-shape
+queries.
+
+The Python wrappers must refuse output tensors that are not on the inputs'
+GPU before anything reaches the library: their raw entry points are replaced
+by stubs that fail the test if called."""
+
+import math
+
+import pytest
+import torch
+
+import exact_attention_67_amd as fa
+
+pytestmark = pytest.mark.gpu
+
+MIB = 1 << 20
+REGIONS = 12  # 1 MiB apart, each much larger than any tensor used below
+
+
+@pytest.fixture()
+def arena():
+    buf = torch.zeros(REGIONS * MIB + 4096, dtype=torch.uint8, device="cuda")
+    base = buf.data_ptr()
+    assert base % 256 == 0
+    yield buf, [base + i * MIB for i in range(REGIONS)]
+    torch.cuda.synchronize()
+    assert int(buf.count_nonzero()) == 0, "a rejected call wrote device memory"
+
+
+def fwd(fn, p, q=None, k=None, v=None, o=None, lse=None, B=1, H=2, S=128, D=64, causal=1,
+        scale=0.125):
+    q = p[0] if q is None else q
+    k = p[1] if k is None else k
+    v = p[2] if v is None else v
+    o = p[3] if o is None else o
+    lse = p[4] if lse is None else lse
+    return fn(q, k, v, o, lse, B, H, S, D, causal, scale, None)
+
+
+@pytest.mark.parametrize("f32", [False, True])
+def test_fwd_rejections_on_real_buffers(arena, f32):
+    _, p = arena
+    fn = fa.fa_fwd_f32 if f32 else fa.fa_fwd
+    n = 1 * 2 * 128 * 64 * (4 if f32 else 2)
+    for s in (0.0, -0.125, math.inf, -math.inf, math.nan):
+        assert fwd(fn, p, scale=s) == fa.FA_ERR_SCALE, s
+    assert fwd(fn, p, q=p[0] + 8) == fa.FA_ERR_ALIGN
+    assert fwd(fn, p, o=p[3] + 4) == fa.FA_ERR_ALIGN
+    assert fwd(fn, p, lse=p[4] + 2) == fa.FA_ERR_ALIGN
+    assert fwd(fn, p, o=p[0]) == fa.FA_ERR_ALIAS
+    assert fwd(fn, p, o=p[1] + n - 16) == fa.FA_ERR_ALIAS
+    assert fwd(fn, p, lse=p[2] + 256) == fa.FA_ERR_ALIAS
+    assert fwd(fn, p, lse=p[3] + n - 4) == fa.FA_ERR_ALIAS
+
+
+def test_fwd_kv_rejections_on_real_buffers(arena):
+    _, p = arena
+
+    def call(q=p[0], k=p[1], v=p[2], o=p[3], lse=p[4], scale=0.125):
+        return fa.fa_fwd_kv(q, k, v, o, lse, 1, 2, 64, 300, 128, 1, scale, None)
+
+    kbytes = 1 * 2 * 300 * 128 * 2
+    qbytes = 1 * 2 * 64 * 128 * 2
+    assert call(scale=math.nan) == fa.FA_ERR_SCALE
+    assert call(scale=-1.0) == fa.FA_ERR_SCALE
+    assert call(k=p[1] + 8) == fa.FA_ERR_ALIGN
+    assert call(lse=p[4] + 1) == fa.FA_ERR_ALIGN
+    assert call(o=p[1] + kbytes - 16) == fa.FA_ERR_ALIAS
+    assert call(lse=p[0] + qbytes - 4) == fa.FA_ERR_ALIAS
+
+
+def test_merge_rejections_on_real_buffers(arena):
+    _, p = arena
+
+    def call(op=p[0], lp=p[1], o=p[2], lse=p[3]):
+        return fa.fa_merge(op, lp, 3, 1, 2, 100, 64, o, lse, None)
+
+    parts = 3 * 1 * 2 * 100 * 64 * 2
+    assert call(op=p[0] + 8) == fa.FA_ERR_ALIGN
+    assert call(o=p[2] + 8) == fa.FA_ERR_ALIGN
+    assert call(lse=p[3] + 2) == fa.FA_ERR_ALIGN
+    assert call(o=p[0] + parts - 16) == fa.FA_ERR_ALIAS
+    assert call(lse=p[1] + 4) == fa.FA_ERR_ALIAS
+    assert call(o=p[2], lse=p[2] + 64) == fa.FA_ERR_ALIAS
+
+
+def test_bwd_rejections_on_real_buffers(arena):
+    _, p = arena
+    names = ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv", "delta")
+
+    def call(scale=0.125, **kw):
+        a = dict(zip(names, p[:10]))
+        a.update(kw)
+        return fa.fa_bwd(*(a[n] for n in names), 1, 2, 100, 128, 1, scale, None)
+
+    nb = 1 * 2 * 100 * 128 * 2
+    for s in (0.0, -1.0, math.nan, math.inf):
+        assert call(scale=s) == fa.FA_ERR_SCALE, s
+    assert call(dk=p[7] + 8) == fa.FA_ERR_ALIGN
+    assert call(delta=p[9] + 2) == fa.FA_ERR_ALIGN
+    assert call(dq=p[0] + nb - 16) == fa.FA_ERR_ALIAS
+    assert call(dv=p[6] + 16) == fa.FA_ERR_ALIAS
+    assert call(delta=p[5]) == fa.FA_ERR_ALIAS
+
+
+# ---------------------------------------------------------------------------
+# Wrappers: outputs must be on the inputs' GPU; nothing reaches the library
+# ---------------------------------------------------------------------------
+
+@pytest.fixture()
+def no_launch(monkeypatch):
+    def stub(*a, **k):
+        raise AssertionError("the raw entry point was called")
+    for name in ("fa_fwd", "fa_fwd_f32", "fa_fwd_kv", "fa_merge", "fa_bwd"):
+        monkeypatch.setattr(fa, name, stub)
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+def test_forward_refuses_host_outputs(no_launch, dt):
+    q = torch.zeros(1, 2, 64, 64, dtype=dt, device="cuda")
+    good_o, good_l = torch.empty_like(q), torch.empty(1, 2, 64, device="cuda")
+    with pytest.raises(ValueError):
+        fa.forward(q, q, q, out=torch.empty_like(q, device="cpu"), lse=good_l)
+    with pytest.raises(ValueError):
+        fa.forward(q, q, q, out=good_o, lse=torch.empty(1, 2, 64))
+    with pytest.raises(ValueError):
+        fa.forward(q, q.cpu(), q)
+
+
+def test_forward_kv_refuses_host_outputs(no_launch):
+    q = torch.zeros(1, 2, 8, 128, dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros(1, 2, 40, 128, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        fa.forward_kv(q, k, k, out=torch.empty(1, 2, 8, 128, dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        fa.forward_kv(q, k, k, lse=torch.empty(1, 2, 8))
+
+
+def test_merge_refuses_host_outputs(no_launch):
+    op = torch.zeros(2, 1, 1, 8, 64, dtype=torch.bfloat16, device="cuda")
+    lp = torch.zeros(2, 1, 1, 8, dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError):
+        fa.merge(op, lp, out=torch.empty(1, 1, 8, 64, dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        fa.merge(op, lp, lse=torch.empty(1, 1, 8))
+    with pytest.raises(ValueError):
+        fa.merge(op, lp.cpu())
+
+
+def test_backward_refuses_host_inputs(no_launch):
+    q = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16, device="cuda")
+    lse = torch.zeros(1, 1, 64, device="cuda")
+    with pytest.raises(ValueError):
+        fa.backward(q, q, q, q, q, lse.cpu())
+    with pytest.raises(ValueError):
+        fa.backward(q, q, q, q.cpu(), q, lse)
