@@ -25,6 +25,8 @@ from ._lib import (  # noqa: F401
     FA_ERR_HEADDIM,
     FA_ERR_LAUNCH,
     FA_ERR_NULL,
+    FA_ERR_SCRATCH,
+    FA_BWD_SCRATCH_ROWS,
     FA_ERR_SCALE,
     FA_ERR_SHAPE,
     FA_OK,
@@ -32,6 +34,7 @@ from ._lib import (  # noqa: F401
     FAError,
     fa_fwd,
     fa_bwd,
+    fa_bwd_noalloc,
     fa_fwd_f32,
     fa_fwd_kv,
     fa_fwd_kv_plan,
@@ -42,7 +45,7 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = ["forward", "forward_kv", "merge", "backward", "fa_fwd", "fa_fwd_f32", "fa_fwd_kv",
-           "fa_merge", "fa_bwd", "fa_fwd_plan", "fa_fwd_kv_plan", "load", "status_str",
+           "fa_merge", "fa_bwd", "fa_bwd_noalloc", "fa_fwd_plan", "fa_fwd_kv_plan", "load", "status_str",
            "FAError"]
 
 

@@ -25,9 +25,11 @@ FA_ERR_CAUSAL = 5
 FA_ERR_ALIGN = 6
 FA_ERR_ALIAS = 7
 FA_ERR_LAUNCH = 8
+FA_ERR_SCRATCH = 9
+FA_BWD_SCRATCH_ROWS = 1 << 21
 
-EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_kv", "fa_merge", "fa_bwd", "fa_fwd_plan",
-           "fa_fwd_kv_plan", "fa_status_str", "fa_abi_version")
+EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_kv", "fa_merge", "fa_bwd", "fa_bwd_noalloc",
+           "fa_fwd_plan", "fa_fwd_kv_plan", "fa_status_str", "fa_abi_version")
 ABI_VERSION = 1
 
 _lock = threading.Lock()
@@ -55,6 +57,8 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.fa_merge.restype = i
     lib.fa_bwd.argtypes = [vp] * 10 + [i, i, i, i, i, f, vp]
     lib.fa_bwd.restype = i
+    lib.fa_bwd_noalloc.argtypes = [vp] * 9 + [i, i, i, i, i, f, vp]
+    lib.fa_bwd_noalloc.restype = i
     ip = ctypes.POINTER(i)
     lib.fa_fwd_plan.argtypes = [i, i, i, i, i, i, ip, ip, ip, ip]
     lib.fa_fwd_plan.restype = i
@@ -120,6 +124,15 @@ def fa_bwd(q: int, k: int, v: int, o: int, dout: int, lse: int, dq: int, dk: int
     """Raw C call on device addresses (ints).  Returns the fa_status."""
     return load().fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, S, D, causal, scale,
                          stream)
+
+
+def fa_bwd_noalloc(q: int, k: int, v: int, o: int, dout: int, lse: int, dq: int, dk: int,
+                   dv: int, B: int, H: int, S: int, D: int, causal: int, scale: float,
+                   stream: int | None) -> int:
+    """Raw C call on device addresses (ints); Delta in the library's fixed
+    scratch array (no allocation).  Returns the fa_status."""
+    return load().fa_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, B, H, S, D, causal, scale,
+                                 stream)
 
 
 def fa_fwd_plan(B: int, H: int, S: int, D: int, causal: int, elem_bytes: int) -> dict:

@@ -36,12 +36,15 @@
 //    transposed.  K and V tiles are stored in one swizzle that serves both the
 //    row reads and the transposing reads, so each K tile is copied once.
 // No atomics and no workspace beyond the caller's Delta buffer: dq is
-// accumulated by the workgroup that owns the query tile.
+// accumulated by the workgroup that owns the query tile.  fa_bwd_noalloc
+// keeps Delta in a fixed device array of the library instead (scratch below).
 
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+
+#include <atomic>
 
 #include "fa.h"
 #include "fa_device.h"
@@ -605,11 +608,13 @@ int run_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint1
 
 }  // namespace
 
-extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o,
-                      const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                      float* delta, int B, int H, int S, int D, int causal, float scale,
-                      void* stream) {
-  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !delta) return FA_ERR_NULL;
+// Argument checks shared by fa_bwd and fa_bwd_noalloc.  delta is the caller's
+// Delta buffer, or NULL when the library's scratch array holds Delta.
+int validate_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, float* delta, bool own_delta,
+                 int B, int H, int S, int D, int causal, float scale) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || (!own_delta && !delta))
+    return FA_ERR_NULL;
   if (B < 1 || H < 1 || S < 1) return FA_ERR_SHAPE;
   if (D != 64 && D != 128 && D != 256) return FA_ERR_HEADDIM;
   if (causal != 0 && causal != 1) return FA_ERR_CAUSAL;
@@ -627,12 +632,20 @@ extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o
   const size_t in_b[6] = {tb, tb, tb, tb, tb, lb};
   void* outs[4] = {dq, dk, dv, delta};
   const size_t out_b[4] = {tb, tb, tb, lb};
-  for (int a = 0; a < 4; ++a) {
+  const int nout = own_delta ? 3 : 4;
+  for (int a = 0; a < nout; ++a) {
     for (int i = 0; i < 6; ++i)
       if (overlap(outs[a], out_b[a], ins[i], in_b[i])) return FA_ERR_ALIAS;
-    for (int b = a + 1; b < 4; ++b)
+    for (int b = a + 1; b < nout; ++b)
       if (overlap(outs[a], out_b[a], outs[b], out_b[b])) return FA_ERR_ALIAS;
   }
+  return FA_OK;
+}
+
+int bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+        const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int H, int S,
+        int D, int causal, float scale, void* stream) {
+  const int64_t bh = (int64_t)B * H;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const auto* Q = static_cast<const uint16_t*>(q);
   const auto* Kp = static_cast<const uint16_t*>(k);
@@ -647,4 +660,61 @@ extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o
   if (D == 128)
     return run_bwd<128>(Q, Kp, Vp, O, dO, lse, dQ, dK, dV, delta, (int)bh, S, causal != 0, scale, s);
   return run_bwd<256>(Q, Kp, Vp, O, dO, lse, dQ, dK, dV, delta, (int)bh, S, causal != 0, scale, s);
+}
+
+// Delta of fa_bwd_noalloc: one float per query row, at most FA_BWD_SCRATCH_ROWS
+// rows per call.  Every row a call uses is written by fa_bwd_delta_kernel
+// before the other kernels of that call read it, so nothing needs clearing.
+// Each GPU holds its own copy of the array, at its own address, for the life
+// of the process; host code uses that address (scratch_address), never the
+// array's name, which on the host only stands in for the device symbol.
+static __device__ __align__(256) float scratch[FA_BWD_SCRATCH_ROWS];
+
+constexpr int kMaxDevices = 64;
+std::atomic<float*> g_scratch[kMaxDevices];  // device address of scratch, per device
+
+// Address of scratch on the device `stream` runs on, looked up once per
+// device with that device current.
+int scratch_address(hipStream_t stream, float** out) {
+  int dev = -1;
+  const hipError_t ge = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (ge != hipSuccess || dev < 0 || dev >= kMaxDevices) return FA_ERR_LAUNCH;
+  float* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return FA_ERR_LAUNCH;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return FA_ERR_LAUNCH;
+    void* addr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+    if (cur != dev && hipSetDevice(cur) != hipSuccess) return FA_ERR_LAUNCH;
+    if (e != hipSuccess || !addr) return FA_ERR_LAUNCH;
+    p = static_cast<float*>(addr);
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return FA_OK;
+}
+
+extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o,
+                      const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                      float* delta, int B, int H, int S, int D, int causal, float scale,
+                      void* stream) {
+  const int st = validate_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, false, B, H, S, D,
+                              causal, scale);
+  if (st != FA_OK) return st;
+  return bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, S, D, causal, scale, stream);
+}
+
+extern "C" int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                              const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                              int B, int H, int S, int D, int causal, float scale,
+                              void* stream) {
+  int st = validate_bwd(q, k, v, o, dout, lse, dq, dk, dv, nullptr, true, B, H, S, D, causal,
+                        scale);
+  if (st != FA_OK) return st;
+  if ((int64_t)B * H * S > (int64_t)FA_BWD_SCRATCH_ROWS) return FA_ERR_SCRATCH;
+  float* delta = nullptr;
+  st = scratch_address(static_cast<hipStream_t>(stream), &delta);
+  if (st != FA_OK) return st;
+  return bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, S, D, causal, scale, stream);
 }

@@ -1247,6 +1247,7 @@ extern "C" const char* fa_status_str(int status) {
     case FA_ERR_ALIGN: return "q/k/v/o must be 16-byte aligned and lse 4-byte aligned";
     case FA_ERR_ALIAS: return "o or lse overlaps an input or each other";
     case FA_ERR_LAUNCH: return "kernel launch failed";
+    case FA_ERR_SCRATCH: return "B*H*S exceeds the library's backward scratch array";
     default: return "unknown status";
   }
 }

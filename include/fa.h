@@ -58,8 +58,13 @@ enum fa_status {
     FA_ERR_CAUSAL  = 5, /* causal not 0 or 1 */
     FA_ERR_ALIGN   = 6, /* q/k/v/o not 16-byte aligned or lse not 4-byte aligned */
     FA_ERR_ALIAS   = 7, /* o or lse overlaps an input or each other */
-    FA_ERR_LAUNCH  = 8  /* the HIP launch itself failed */
+    FA_ERR_LAUNCH  = 8, /* the HIP launch (or a HIP query before it) failed */
+    FA_ERR_SCRATCH = 9  /* fa_bwd_noalloc: B*H*S above FA_BWD_SCRATCH_ROWS */
 };
+
+/* Rows (B*H*S) the library's fixed backward scratch array holds: one float32
+ * per row, 8 MiB on each GPU the library runs fa_bwd_noalloc on. */
+#define FA_BWD_SCRATCH_ROWS (1 << 21)
 
 /*
  * fa_fwd -- bf16 attention forward.
@@ -157,6 +162,23 @@ int fa_merge(const void* o_parts, const float* lse_parts, int G, int B, int H, i
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
            const float* lse, void* dq, void* dk, void* dv, float* delta,
            int B, int H, int S, int D, int causal, float scale, void* stream);
+
+/*
+ * fa_bwd_noalloc -- fa_bwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, results and errors as fa_bwd without the delta
+ * buffer: Delta lives in a fixed device array of the library (8 MiB per GPU,
+ * held until the process ends), so the call allocates nothing and only
+ * enqueues the same kernels.  B*H*S must be at most FA_BWD_SCRATCH_ROWS, else
+ * FA_ERR_SCRATCH (nothing enqueued).  The first call on a GPU looks up the
+ * array's address there (FA_ERR_LAUNCH if that fails).  All calls on one GPU
+ * share its array: calls that overlap in time on one GPU (different streams
+ * without ordering between them) race on it and give wrong results; calls
+ * ordered on one stream are safe.
+ */
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                   const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                   int B, int H, int S, int D, int causal, float scale, void* stream);
 
 /*
  * fa_fwd_plan -- the launch shape fa_fwd (elem_bytes = 2) or fa_fwd_f32

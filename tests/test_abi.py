@@ -41,7 +41,7 @@ def test_library_loads_and_exports_every_header_symbol():
 
 
 def test_status_strings():
-    for st in range(0, 9):
+    for st in range(0, 10):
         s = fa.status_str(st)
         assert s and s != "unknown status"
     assert fa.status_str(12345) == "unknown status"
@@ -187,6 +187,38 @@ def test_bwd_validation_errors():
     assert call_bwd(dv=A * 7 + 16) == fa.FA_ERR_ALIAS         # dv overlaps dq
     assert call_bwd(delta=A * 6) == fa.FA_ERR_ALIAS           # delta overlaps lse
     assert call_bwd(dq=Q + nb, causal=3) == fa.FA_ERR_CAUSAL  # adjacent: no alias
+
+
+def call_bwd_noalloc(**kw):
+    base = dict(q=Q, k=K, v=V, o=O, do=L, lse=A * 6, dq=A * 7, dk=A * 8, dv=A * 9,
+                B=1, H=2, S=100, D=128, causal=1, scale=0.125)
+    base.update(kw)
+    b = base
+    return fa.fa_bwd_noalloc(b["q"], b["k"], b["v"], b["o"], b["do"], b["lse"], b["dq"],
+                             b["dk"], b["dv"], b["B"], b["H"], b["S"], b["D"], b["causal"],
+                             b["scale"], None)
+
+
+@no_device
+def test_bwd_noalloc_validation_errors():
+    for name in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv"):
+        assert call_bwd_noalloc(**{name: 0}) == fa.FA_ERR_NULL, name
+    assert call_bwd_noalloc(S=0) == fa.FA_ERR_SHAPE
+    assert call_bwd_noalloc(D=96) == fa.FA_ERR_HEADDIM
+    assert call_bwd_noalloc(causal=2) == fa.FA_ERR_CAUSAL
+    assert call_bwd_noalloc(scale=math.nan) == fa.FA_ERR_SCALE
+    assert call_bwd_noalloc(dv=A * 9 + 8) == fa.FA_ERR_ALIGN
+    assert call_bwd_noalloc(dq=Q + 16) == fa.FA_ERR_ALIAS
+    # more rows than the fixed scratch array holds: rejected before any HIP call
+    rows = fa.FA_BWD_SCRATCH_ROWS
+    assert call_bwd_noalloc(B=1, H=1, S=rows + 1, D=64) == fa.FA_ERR_SCRATCH
+    assert call_bwd_noalloc(B=2, H=3, S=rows // 6 + 1, D=64) == fa.FA_ERR_SCRATCH
+
+
+def test_scratch_limit_matches_header():
+    src = open(HEADER).read()
+    m = re.search(r"#define\s+FA_BWD_SCRATCH_ROWS\s+\(1\s*<<\s*(\d+)\)", src)
+    assert m and fa.FA_BWD_SCRATCH_ROWS == 1 << int(m.group(1))
 
 
 def test_forward_rejects_cpu_tensors():
