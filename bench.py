@@ -282,6 +282,72 @@ def time_secondary(steps):
     return out
 
 
+# The tile-pipeline study (the "Pipelining GmemCopy on kHeadDim" issue's
+# questions): the bf16 forward with its K/V tiles copied one step ahead (the
+# library), copied and waited for in the step that reads them, or copied two
+# or three steps ahead into three or four buffers each, and the products with
+# their operand reads alone (no copies, no exponentials).
+STUDY_WORKLOADS = (("c4_bf16_causal_1x32x16384x128", True), ("c3_bf16_2x16x4096x128", True),
+                   ("c3_bf16_2x16x4096x128", False))
+
+
+def pipeline_study(rounds=3):
+    """TFLOP/s of each pipeline-study build against the library on the same
+    inputs, alternating builds within each round (median over rounds)."""
+    import ctypes
+    import torch
+    import exact_attention_67_amd as fa
+    from exact_attention_67_amd import _lib
+    from tests import workloads as wl
+
+    libs = {"overlap (library)": fa.load()}
+    for name in _lib.PIPE_VARIANTS:
+        libs[name] = _lib.load_variant(name)
+    stream = torch.cuda.current_stream()
+    out = {}
+    for name, causal in STUDY_WORKLOADS:
+        w = wl.WORKLOADS[name]
+        q, k, v = wl.make_inputs(w, device="cuda")
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device="cuda")
+        args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                w.B, w.H, w.S, w.D, int(causal), ctypes.c_float(w.scale), stream.cuda_stream)
+        flops = w.flops(causal)
+        times = {n: [] for n in libs}
+        for r in range(rounds):
+            for n, lib in libs.items():
+                def launch():
+                    st = lib.fa_fwd(*args)
+                    if st != fa.FA_OK:
+                        raise fa.FAError(st, f"fa_fwd ({n})")
+                launch()
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                launch()
+                torch.cuda.synchronize()
+                one = max(time.perf_counter() - t0, 1e-5)
+                for _ in range(max(2, int(0.1 / one))):   # ~100 ms of warm-up
+                    launch()
+                n_t = max(5, int(0.05 / one))             # ~50 ms timed
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(n_t):
+                    launch()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                times[n].append(e0.elapsed_time(e1) / n_t)
+        key = f"{name}_{'causal' if causal else 'full'}"
+        out[key] = {}
+        for n in libs:
+            ms = sorted(times[n])[len(times[n]) // 2]
+            out[key][n] = {"ms": round(ms, 5), "tflops": round(flops / (ms * 1e-3) / 1e12, 1)}
+        log(f"[study] {key}: " + "  ".join(f"{n} {out[key][n]['tflops']}" for n in libs))
+        del q, k, v, o, lse
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(w, causal, budget_s=20.0):
     """The oracle, as it stands, on the host cores over a bounded sample of the
     same workload: whole heads (row-blocked), one after another until the time
@@ -348,6 +414,9 @@ def main():
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the cold-cache launches (profiling runs count warm launches only)")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--pipeline-study", action="store_true",
+                    help="also time the tile-pipeline study builds against the library "
+                         "(TFLOP/s table on stderr, 'pipeline_study' in the JSON line)")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     a = ap.parse_args()
 
@@ -376,6 +445,7 @@ def main():
     # an idle gap (see the module docstring).
     inputs = wl.make_inputs(w, device="cuda")
     secondary = None if a.no_secondary else time_secondary(max(5, a.steps // 5))
+    study = pipeline_study() if a.pipeline_study else None
 
     log(f"[bench] {w.name} causal={causal} steps={a.steps} warmup={a.warmup}")
     r = time_workload(w, causal, a.steps, a.warmup,
@@ -464,6 +534,9 @@ def main():
         # path, the merge and the backward pass, each on its own workloads
         "secondary": secondary,
     }
+    if study is not None:
+        # not part of `value`: the tile-pipeline study builds, same inputs
+        line["pipeline_study"] = study
     if rank == 0:
         print(json.dumps(line), flush=True)
 

@@ -32,8 +32,32 @@ EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_kv", "fa_merge", "fa_bwd", "fa_bwd_no
            "fa_fwd_plan", "fa_fwd_kv_plan", "fa_status_str", "fa_abi_version")
 ABI_VERSION = 1
 
+# Pipeline-study builds of the same library: the bf16 forward's K/V tile
+# pipeline in another mode (FA_PIPE at build time; see the pipeline modes in
+# csrc/fa_fwd.hip).  Everything else is the same code.
+PIPE_VARIANTS = {"noprefetch": 1, "ring3": 3, "ring4": 4, "mfma_only": 5}
+
 _lock = threading.Lock()
 _lib = None
+_variants = {}
+
+
+def variant_path(name: str) -> str:
+    if name not in PIPE_VARIANTS:
+        raise ValueError(f"unknown pipeline variant {name!r} (one of {sorted(PIPE_VARIANTS)})")
+    return os.path.join(PKG, f"libfa_mi355x_pipe_{name}.so")
+
+
+def load_variant(name: str) -> ctypes.CDLL:
+    """Load (once) a pipeline-study build; raises if it is not built."""
+    p = variant_path(name)
+    with _lock:
+        if name in _variants:
+            return _variants[name]
+    lib = load(p)
+    with _lock:
+        _variants[name] = lib
+    return lib
 
 
 class FAError(RuntimeError):

@@ -1,7 +1,9 @@
 """Build the HIP library in-tree: exact_attention_67_amd/libfa_mi355x.so.
 
 Compiles the HIP sources in csrc/ (forward and backward kernels, host entry
-points) into one shared library, for gfx950 only, with hipcc.  Packed-fp32 code
+points) into one shared library, for gfx950 only, with hipcc, and the same
+sources with the bf16 forward's tile pipeline in its study modes into
+libfa_mi355x_pipe_<name>.so (in parallel).  Packed-fp32 code
 generation is switched off for device code (the host pass warns that it does
 not know the feature; that warning is harmless).
 
@@ -46,25 +48,42 @@ def compile_flags() -> list:
     ]
 
 
-def build(verbose: bool = False, save_temps: str | None = None) -> str:
-    """Compile the library; always recompiles.  Returns the .so path."""
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), *compile_flags(), "-shared", *[src for src in SOURCES if os.path.exists(src)],
-           "-o", tmp]
+def _compile(out_path: str, defines: list, verbose: bool, save_temps: str | None):
+    tmp = out_path + ".tmp"
+    cmd = [hipcc(), *compile_flags(), *defines, "-shared",
+           *[src for src in SOURCES if os.path.exists(src)], "-o", tmp]
     if save_temps:
         os.makedirs(save_temps, exist_ok=True)
         cmd.insert(1, "-save-temps=cwd")
         cmd.insert(1, "-Rpass-analysis=kernel-resource-usage")
     if verbose:
         print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True,
-                         cwd=save_temps if save_temps else PKG)
-    if res.returncode != 0:
-        sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
-    if verbose and (res.stdout or res.stderr):
-        sys.stderr.write(res.stdout + res.stderr)
-    os.replace(tmp, LIB_PATH)
+    proc = subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True,
+                            cwd=save_temps if save_temps else PKG)
+    return proc, tmp, out_path
+
+
+def build(verbose: bool = False, save_temps: str | None = None, variants: bool = True) -> str:
+    """Compile the library (and, unless variants=False, the pipeline-study
+    builds of it) for gfx950; always recompiles.  Returns the library path."""
+    from ._lib import PIPE_VARIANTS, variant_path
+
+    jobs = [_compile(LIB_PATH, [], verbose, save_temps)]
+    if variants and not save_temps:
+        for name, mode in PIPE_VARIANTS.items():
+            jobs.append(_compile(variant_path(name), [f"-DFA_PIPE={mode}"], verbose, None))
+    failed = []
+    for proc, tmp, out_path in jobs:
+        out, _ = proc.communicate()
+        if proc.returncode != 0:
+            sys.stderr.write(out)
+            failed.append((out_path, proc.returncode))
+            continue
+        if verbose and out:
+            sys.stderr.write(out)
+        os.replace(tmp, out_path)
+    if failed:
+        raise RuntimeError(f"hipcc failed: {failed}")
     return LIB_PATH
 
 
@@ -73,8 +92,10 @@ def main() -> None:
     ap.add_argument("--verbose", action="store_true")
     ap.add_argument("--save-temps", default=None,
                     help="directory to keep intermediate files (ISA) and resource usage")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="build only the library, not its pipeline-study builds")
     a = ap.parse_args()
-    print(build(verbose=a.verbose, save_temps=a.save_temps))
+    print(build(verbose=a.verbose, save_temps=a.save_temps, variants=not a.no_variants))
 
 
 if __name__ == "__main__":

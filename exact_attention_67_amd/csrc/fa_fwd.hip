@@ -66,6 +66,39 @@ constexpr int kBr = kRowsPerWave * kWaves;  // float32 kernel: query rows per wo
 #endif
 constexpr bool kMfmaSum = FA_MFMA_SUM != 0;  // bf16-weight sums on the matrix cores
 
+// s_waitcnt immediate: at most n vector-memory operations outstanding, all
+// LDS operations done (expcnt untouched).
+constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
+
+// How fa_fwd_bf16_kernel moves K/V tiles into LDS.  The library's fa_fwd uses
+// kPipeOverlap; the other modes exist for the pipelining study of the
+// "Pipelining GmemCopy on kHeadDim" issue (whole-tile prefetch against none,
+// and deeper buffering) and are compiled only into separate study libraries
+// (FA_PIPE at build time).
+enum PipeMode : int {
+  kPipeOverlap = 0,     // a tile is copied during the step before it is read; two buffers each
+  kPipeNoPrefetch = 1,  // each step copies the tiles it reads, waits for them, then computes
+  kPipeRing3 = 3,       // three buffers each; a tile is copied two steps before it is read
+  kPipeRing4 = 4,       // four buffers each; a tile is copied three steps before it is read
+  kPipeMfmaOnly = 5,    // no copies, no exponentials, no weight check: the products and
+                        // their LDS operand reads alone (a timing probe; results are void)
+};
+template <int PIPE>
+struct PipeCfg {
+  static constexpr int R = PIPE == kPipeRing3 ? 3 : PIPE == kPipeRing4 ? 4 : 2;  // buffers each
+  static constexpr int U = R == 3 ? 6 : R;  // steps per unrolled group: buffer slots and S parity
+  static constexpr bool kPrefetch = PIPE != kPipeNoPrefetch;
+  static constexpr bool kCopies = PIPE != kPipeMfmaOnly;
+  static constexpr bool kSoftmax = PIPE != kPipeMfmaOnly;
+};
+#ifndef FA_PIPE
+#define FA_PIPE 0
+#endif
+constexpr int kPipe = FA_PIPE;
+static_assert(kPipe == kPipeOverlap || kPipe == kPipeNoPrefetch || kPipe == kPipeRing3 ||
+                  kPipe == kPipeRing4 || kPipe == kPipeMfmaOnly,
+              "FA_PIPE");
+
 // sched_group_barrier with a compile-time count; nothing when the count is 0.
 template <int MASK, int N>
 __device__ __forceinline__ void sched_group() {
@@ -127,24 +160,46 @@ __device__ __forceinline__ void step_schedule(std::integer_sequence<int, I...>) 
 // rescales (weights stay <= kRowSumLimit, so nothing overflows).  The
 // reference is set from the true max of tile 0 before the first step, and it
 // only moves up, so the largest weight of a row is >= 1.
-template <int D, int BC, int WAVES, bool CAUSAL, bool MFMA_SUM>
+template <int D, int BC, int WAVES, bool CAUSAL, bool MFMA_SUM, int PIPE>
 __global__ __launch_bounds__(64 * WAVES, 2) void fa_fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
     int Sq, int Sk, int nq, int bh_total, int group_heads, float c) {
   using C = BfCfg<D, BC, WAVES>;
-  // Four separate buffers (K and V, two each) rather than one array indexed
-  // by tile parity: every access below names its buffer statically, so the
-  // compiler can tell that an asynchronous copy into one buffer never aliases
-  // reads of another and does not make those reads wait for the copy.
+  using PC = PipeCfg<PIPE>;
+  constexpr int R = PC::R, U = PC::U;
+  // Separate buffers (R for K, R for V) rather than one array indexed by tile
+  // number: every access below names its buffer statically (the step code is
+  // unrolled over U consecutive steps), so the compiler can tell that an
+  // asynchronous copy into one buffer never aliases reads of another and does
+  // not make those reads wait for the copy.
   __shared__ __attribute__((aligned(1024))) uint8_t kbuf0_raw[C::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t kbuf1_raw[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf2_raw[R > 2 ? C::TILE_BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf3_raw[R > 3 ? C::TILE_BYTES : 16];
   __shared__ __attribute__((aligned(1024))) uint8_t vbuf0_raw[C::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t vbuf1_raw[C::TILE_BYTES];
-  lds_u8* kbuf0 = (lds_u8*)kbuf0_raw;
-  lds_u8* kbuf1 = (lds_u8*)kbuf1_raw;
-  lds_u8* vbuf0 = (lds_u8*)vbuf0_raw;
-  lds_u8* vbuf1 = (lds_u8*)vbuf1_raw;
+  __shared__ __attribute__((aligned(1024))) uint8_t vbuf2_raw[R > 2 ? C::TILE_BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t vbuf3_raw[R > 3 ? C::TILE_BYTES : 16];
+  // buffer of K (V) tile u, for a compile-time u (only its residue mod R matters)
+  const auto kslot = [&](auto u) -> lds_u8* {
+    constexpr int i = decltype(u)::value % R;
+    if constexpr (i == 0) return (lds_u8*)kbuf0_raw;
+    else if constexpr (i == 1) return (lds_u8*)kbuf1_raw;
+    else if constexpr (i == 2) return (lds_u8*)kbuf2_raw;
+    else return (lds_u8*)kbuf3_raw;
+  };
+  const auto vslot = [&](auto u) -> lds_u8* {
+    constexpr int i = decltype(u)::value % R;
+    if constexpr (i == 0) return (lds_u8*)vbuf0_raw;
+    else if constexpr (i == 1) return (lds_u8*)vbuf1_raw;
+    else if constexpr (i == 2) return (lds_u8*)vbuf2_raw;
+    else return (lds_u8*)vbuf3_raw;
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
 
   int bh, qt;
   decode_tile<CAUSAL>(xcd_logical_index(blockIdx.x, nq * bh_total), nq, bh_total,
@@ -183,10 +238,26 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fa_fwd_bf16_kernel(
   const int cw = copier ? wave : 0;  // this wave's share of each copy
   const CopyLanes cl = copy_lanes<C>(cw, lane);
 
-  // K(0) and K(1) now; step t copies K(t+2) and V(t).
-  if (copier && ntiles > 0) {
-    copy_tile<C, false>(Kh, kbuf0, 0, Sk, cw, lane, cl);
-    if (ntiles > 1) copy_tile<C, false>(Kh, kbuf1, BC, Sk, cw, lane, cl);
+  // With prefetch: K(0) .. K(R-1) and V(0) .. V(R-3) now; step t copies
+  // K(t+R) and V(t+R-2) (so K(t+2) and V(t) with two buffers).  Without:
+  // K(0) now; step t copies K(t+1) and V(t-1).
+  const auto copy_k = [&](int u, lds_u8* dst) { copy_tile<C, false>(Kh, dst, u * BC, Sk, cw, lane, cl); };
+  const auto copy_v = [&](int u, lds_u8* dst) { copy_tile<C, true>(Vh, dst, u * BC, Sk, cw, lane, cl); };
+  if constexpr (PC::kCopies) {
+    if (copier && ntiles > 0) {
+      copy_k(0, kslot(I0{}));
+      if constexpr (PC::kPrefetch) {
+        if (ntiles > 1) copy_k(1, kslot(I1{}));
+        if constexpr (R > 2) {
+          if (ntiles > 2) copy_k(2, kslot(I2{}));
+          copy_v(0, vslot(I0{}));
+        }
+        if constexpr (R > 3) {
+          if (ntiles > 3) copy_k(3, kslot(I3{}));
+          if (ntiles > 1) copy_v(1, vslot(I1{}));
+        }
+      }
+    }
   }
 
   // Q fragments (B operand of S^T = K * Q^T): lane holds Q[my_q][ch*16 + hh*8 .. +8].
@@ -259,10 +330,16 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fa_fwd_bf16_kernel(
     // its use
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
-      const float x0 = fmaf(s[pc >> 1][(pc & 1) * 8 + e], c, -mc);
-      const float x1 = fmaf(s[pc >> 1][(pc & 1) * 8 + e + 1], c, -mc);
-      const float p0 = fast_exp2(x0);
-      const float p1 = fast_exp2(x1);
+      float p0, p1;
+      if constexpr (PC::kSoftmax) {
+        const float x0 = fmaf(s[pc >> 1][(pc & 1) * 8 + e], c, -mc);
+        const float x1 = fmaf(s[pc >> 1][(pc & 1) * 8 + e + 1], c, -mc);
+        p0 = fast_exp2(x0);
+        p1 = fast_exp2(x1);
+      } else {
+        p0 = s[pc >> 1][(pc & 1) * 8 + e];
+        p1 = s[pc >> 1][(pc & 1) * 8 + e + 1];
+      }
       rs += p0;
       rs += p1;
       w[e] = (__bf16)p0;
@@ -333,30 +410,60 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fa_fwd_bf16_kernel(
   if (wave_ntiles > 0) {
     // S(0) and the reference max from it: every row that sees any key sees
     // key 0, so only rows that see nothing keep -inf.
-    qk_tile<C>(s_a, kbuf0, qf, k_off);
+    qk_tile<C>(s_a, kslot(I0{}), qf, k_off);
     if (needs_mask(0)) apply_mask(s_a, 0);
     m_run = row_max<C>(s_a, hh);
   }
-  __syncthreads();  // every wave is done with K(0) before K(2) overwrites it
+  __syncthreads();  // every wave is done with K(0) before a copy overwrites it
 
-  // Step t: reads K(t+1) from k_next and V(t-1) from v_prev; copies K(t+2)
-  // into k_load (K(t)'s buffer) and V(t) into v_load (V(t-2)'s buffer).
-  // S(t) is in s_in; S(t+1) goes to s_out.  Three kinds of step:
+  // Step t: reads K(t+1) from k_next and V(t-1) from v_prev, and copies
+  // tiles as the pipeline mode says.  S(t) is in s_in; S(t+1) goes to s_out.
+  // Three kinds of step:
   //  kFirst (t = 0):    weights of tile 0, S(1) if the wave needs tile 1;
   //  kFull  (1 <= t, t + 1 < wave_ntiles): P*V of t-1, weights of t, S(t+1),
   //                     under a fixed instruction order;
   //  kTail  (the wave's last steps): P*V of t-1 if the wave has it, weights
   //                     of t if the wave has tile t, no S.
   // Every path gives the weights and S buffers defined values, so that their
-  // previous contents are not kept alive across a step.
+  // previous contents are not kept alive across a step.  The step's position
+  // in a group of U steps (PH = t mod U) names its buffers.
   constexpr int kFirst = 0, kFull = 1, kTail = 2;
-  auto step = [&](auto kind_tag, const int t, const lds_u8* k_next, lds_u8* k_load,
-                  const lds_u8* v_prev, lds_u8* v_load, f32x16 (&s_in)[C::KB],
-                  f32x16 (&s_out)[C::KB]) {
+  const auto pick = [](auto first_tag, auto& a, auto& b) -> auto& {
+    if constexpr (decltype(first_tag)::value) return a;
+    else return b;
+  };
+  auto step = [&](auto kind_tag, auto ph_tag, const int t) {
     constexpr int KIND = decltype(kind_tag)::value;
-    if (copier) {
-      if (t + 2 < ntiles) copy_tile<C, false>(Kh, k_load, (t + 2) * BC, Sk, cw, lane, cl);
-      if (t < ntiles) copy_tile<C, true>(Vh, v_load, t * BC, Sk, cw, lane, cl);
+    constexpr int PH = decltype(ph_tag)::value;
+    const lds_u8* k_next = kslot(std::integral_constant<int, PH + 1>{});
+    const lds_u8* v_prev = vslot(std::integral_constant<int, PH + U - 1>{});
+    // (chosen at compile time, so that both stay in registers)
+    const std::integral_constant<bool, PH % 2 == 0> even{};
+    f32x16(&s_in)[C::KB] = pick(even, s_a, s_b);
+    f32x16(&s_out)[C::KB] = pick(even, s_b, s_a);
+    if constexpr (PC::kCopies) {
+      if constexpr (PC::kPrefetch) {
+        if (copier) {
+          if constexpr (R == 2) {
+            if (t + 2 < ntiles) copy_k(t + 2, kslot(std::integral_constant<int, PH>{}));
+            if (t < ntiles) copy_v(t, vslot(std::integral_constant<int, PH>{}));
+          } else if (ntiles > 0) {
+            // a fixed number of copies per step (the step-end wait counts
+            // them): past the last tile the last tile is copied again, into
+            // a buffer that no later step reads
+            copy_k(min(t + R, ntiles - 1), kslot(std::integral_constant<int, PH>{}));
+            copy_v(min(t + R - 2, ntiles - 1), vslot(std::integral_constant<int, PH + U - 2>{}));
+          }
+        }
+      } else {
+        if (copier) {
+          if (t + 1 < ntiles) copy_k(t + 1, kslot(std::integral_constant<int, PH + 1>{}));
+          if (t >= 1 && t - 1 < ntiles) copy_v(t - 1, vslot(std::integral_constant<int, PH + U - 1>{}));
+        }
+        // the tiles this step reads have landed, for every wave
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+      }
     }
     const bool do_sm = KIND == kFull || t < wave_ntiles;
     if (KIND != kFirst && do_sm && needs_mask(t * BC)) apply_mask(s_in, t * BC);
@@ -423,41 +530,116 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fa_fwd_bf16_kernel(
         for (int kb = 0; kb < C::KB; ++kb) s_out[kb] = f32x16{};
       }
     }
-    if (do_sm) {
-      // The reference moves only if some weight of this tile is too large
-      // (or not finite); for a row that sees no key all weights are 0.
-      if (__any(!(rs <= kRowSumLimit))) raise_reference(s_in, rs);
-      l_exact += rs;
+    if constexpr (PC::kSoftmax) {
+      if (do_sm) {
+        // The reference moves only if some weight of this tile is too large
+        // (or not finite); for a row that sees no key all weights are 0.
+        if (__any(!(rs <= kRowSumLimit))) raise_reference(s_in, rs);
+        l_exact += rs;
+      }
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    if constexpr (PC::kPrefetch) {
+      // With R buffers the copies of the last R - 2 steps may stay in flight
+      // (the steps after the next one read them); the others have landed.
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(PC::kCopies ? (R - 2) * 2 * C::LOADS_PER_WAVE : 0));
+      __syncthreads();
+    }
   };
   const std::integral_constant<int, kFirst> first{};
   const std::integral_constant<int, kFull> full{};
   const std::integral_constant<int, kTail> tail{};
   // Steps 0 .. ntiles (the last one only finishes P*V of the last tile).  The
-  // full steps run in pairs so that buffer and S parity are static; the tail
-  // steps of the wave follow.  Every wave takes ntiles + 1 steps (barriers).
-  step(first, 0, kbuf1, kbuf0, vbuf1, vbuf0, s_a, s_b);
+  // full steps run in groups of U (static buffers and S parity); the wave's
+  // remaining full steps and its last steps follow.  Every wave takes
+  // ntiles + 1 steps (barriers).
+  step(first, I0{}, 0);
   int t = 1;
-  const int t_tail = max(1, wave_ntiles - 1);  // first tail step
-  for (; t + 1 < t_tail; t += 2) {
-    step(full, t, kbuf0, kbuf1, vbuf0, vbuf1, s_b, s_a);
-    step(full, t + 1, kbuf1, kbuf0, vbuf1, vbuf0, s_a, s_b);
+  const int t_tail = max(1, wave_ntiles - 1);  // first step that is not full
+  for (; t + U <= t_tail; t += U) {
+    step(full, I1{}, t);
+    step(full, std::integral_constant<int, 2 % U>{}, t + 1);
+    if constexpr (U > 2) {
+      step(full, std::integral_constant<int, 3 % U>{}, t + 2);
+      step(full, std::integral_constant<int, 4 % U>{}, t + 3);
+    }
+    if constexpr (U > 4) {
+      step(full, std::integral_constant<int, 5 % U>{}, t + 4);
+      step(full, std::integral_constant<int, 6 % U>{}, t + 5);
+    }
   }
-  if (t < t_tail) {
-    step(full, t, kbuf0, kbuf1, vbuf0, vbuf1, s_b, s_a);
-    ++t;
+  if constexpr (U == 2) {
+    // at most one full step left (t is odd here); tail steps in pairs
+    if (t < t_tail) {
+      step(full, I1{}, t);
+      ++t;
+    }
+    if (!(t & 1) && t <= ntiles) {
+      step(tail, I0{}, t);
+      ++t;
+    }
+    for (; t + 1 <= ntiles; t += 2) {
+      step(tail, I1{}, t);
+      step(tail, I0{}, t + 1);
+    }
+    if (t <= ntiles) step(tail, I1{}, t);
+  } else {
+    // t = 1 (mod U) here: the remaining full steps (fewer than U) keep static
+    // buffers; then S(t) is moved to s_a and the wave's last steps (no S,
+    // buffers chosen at run time; they are few) follow.
+    const auto one_full = [&](auto ph_tag) -> bool {
+      if (t >= t_tail) return false;
+      step(full, ph_tag, t);
+      ++t;
+      return true;
+    };
+    if constexpr (U == 4) {
+      (void)(one_full(I1{}) && one_full(I2{}) && one_full(I3{}));
+    } else {
+      (void)(one_full(I1{}) && one_full(I2{}) && one_full(I3{}) &&
+             one_full(std::integral_constant<int, 4>{}) && one_full(std::integral_constant<int, 5>{}));
+    }
+    if (t & 1) {
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb) s_a[kb] = s_b[kb];
+    }
+    const auto kslot_rt = [&](int i) -> lds_u8* {
+      return i == 0 ? (lds_u8*)kbuf0_raw : i == 1 ? (lds_u8*)kbuf1_raw
+             : i == 2 ? (lds_u8*)kbuf2_raw : (lds_u8*)kbuf3_raw;
+    };
+    const auto vslot_rt = [&](int i) -> lds_u8* {
+      return i == 0 ? (lds_u8*)vbuf0_raw : i == 1 ? (lds_u8*)vbuf1_raw
+             : i == 2 ? (lds_u8*)vbuf2_raw : (lds_u8*)vbuf3_raw;
+    };
+    for (; t <= ntiles; ++t) {
+      if (copier && ntiles > 0) {
+        copy_k(min(t + R, ntiles - 1), kslot_rt(t % R));
+        copy_v(min(t + R - 2, ntiles - 1), vslot_rt((t + R - 2) % R));
+      }
+      const bool do_sm = t < wave_ntiles;
+      if (do_sm && needs_mask(t * BC)) apply_mask(s_a, t * BC);
+      const float mc = ref_mc();
+      float rs = 0.0f;
+      if (t - 1 < wave_ntiles) {
+        weight_sums();
+        const lds_u8* v_prev = vslot_rt((t - 1) % R);
+#pragma unroll
+        for (int pc = 0; pc < C::PCH; ++pc) pv_chunk(v_prev, pc);
+      }
+      if (do_sm) {
+#pragma unroll
+        for (int pc = 0; pc < C::PCH; ++pc) pf[pc] = weights(s_a, pc, mc, rs);
+        if (__any(!(rs <= kRowSumLimit))) raise_reference(s_a, rs);
+        l_exact += rs;
+      } else {
+#pragma unroll
+        for (int pc = 0; pc < C::PCH; ++pc) pf[pc] = bf16x8{};
+      }
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0((R - 2) * 2 * C::LOADS_PER_WAVE));
+      __syncthreads();
+    }
+    // no copy into this workgroup's LDS is still in flight when it ends
+    __builtin_amdgcn_s_waitcnt(0);
   }
-  if (!(t & 1) && t <= ntiles) {
-    step(tail, t, kbuf1, kbuf0, vbuf1, vbuf0, s_a, s_b);
-    ++t;
-  }
-  for (; t + 1 <= ntiles; t += 2) {
-    step(tail, t, kbuf0, kbuf1, vbuf0, vbuf1, s_b, s_a);
-    step(tail, t + 1, kbuf1, kbuf0, vbuf1, vbuf0, s_a, s_b);
-  }
-  if (t <= ntiles) step(tail, t, kbuf0, kbuf1, vbuf0, vbuf1, s_b, s_a);
 
   const float le = l_exact + swap_halves(l_exact, hh);
   const float lr = MFMA_SUM ? l_mfma[0] : l_round + swap_halves(l_round, hh);
@@ -521,10 +703,6 @@ __device__ __forceinline__ void plain_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
 }
-
-// s_waitcnt immediate: at most n vector-memory operations outstanding, all
-// LDS operations done (expcnt untouched).
-constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
 
 // ----------------------------------------------------------------------------
 // bf16 kernel with a four-deep K/V ring (used at D = 256)
@@ -1059,9 +1237,9 @@ int run_bf16(const void* q, const void* k, const void* v, void* o, float* lse, i
                   V, Out, lse, Sq, Sk, cfg.nq, p.bh_total, p.group_heads, p.c);
   } else {
     if (causal)
-      return launch(fa_fwd_bf16_kernel<D, BC, WAVES, true, kMfmaSum>, cfg.grid, 64 * WAVES, stream,
+      return launch(fa_fwd_bf16_kernel<D, BC, WAVES, true, kMfmaSum, kPipe>, cfg.grid, 64 * WAVES, stream,
                     Q, K, V, Out, lse, Sq, Sk, cfg.nq, p.bh_total, p.group_heads, p.c);
-    return launch(fa_fwd_bf16_kernel<D, BC, WAVES, false, kMfmaSum>, cfg.grid, 64 * WAVES, stream,
+    return launch(fa_fwd_bf16_kernel<D, BC, WAVES, false, kMfmaSum, kPipe>, cfg.grid, 64 * WAVES, stream,
                   Q, K, V, Out, lse, Sq, Sk, cfg.nq, p.bh_total, p.group_heads, p.c);
   }
 }
