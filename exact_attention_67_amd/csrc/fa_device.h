@@ -78,9 +78,12 @@ typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 
-// A row's reference max is only raised when its running max exceeds it by
-// more than this many powers of two, so softmax weights stay <= 2^8.
-constexpr float kRescaleThreshold = 8.0f;
+// D = 256: a row's reference max is only raised when a tile's max exceeds it
+// by more than this many powers of two, so softmax weights stay <= 2^24 (their
+// float32 sums and the O accumulator stay far from overflow, and a bf16
+// weight keeps its relative precision at any magnitude).  A large margin
+// keeps the raises rare even for rows whose scores spread widely.
+constexpr float kRescaleThreshold = 24.0f;
 // Largest sum of one lane's softmax weights in a tile (32 keys) that the
 // kernels accept without moving the row's reference max.
 constexpr float kRowSumLimit = 4096.0f;

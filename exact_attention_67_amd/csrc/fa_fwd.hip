@@ -35,8 +35,9 @@
 //    128: a lane's sum of weights in the tile above 2^12, found after the
 //    weights are formed, with P*V deferred by one tile so that it only ever
 //    sees checked weights; D = 256: the tile's row max above the reference by
-//    more than 8 powers of two), so the rescale of the O accumulator (a
-//    wave-uniform branch) runs on few tiles.  O is normalised by the sum of
+//    more than 24 powers of two, checked before the tile's work, with the
+//    rescale outside the loop of tiles), so the rescale of the O accumulator
+//    (wave-uniform) runs on few tiles.  O is normalised by the sum of
 //    the bf16 weights that multiplied V (for D <= 128 formed on the matrix
 //    cores by a 16x16x32 product with a 0/1 operand).
 //  * The 1-D grid is decoded XCD-aware (the 8 XCDs receive workgroups round-
@@ -713,7 +714,11 @@ __device__ __forceinline__ void plain_barrier() {
 // This variant keeps four K and four V buffers, issues each tile's copies in
 // the middle of the matrix-core work two tiles ahead of use, and at the end of
 // a tile waits only for the copies of the previous tile.  Same arithmetic,
-// tiling, masking and softmax as fa_fwd_bf16_kernel.
+// tiling and masking as fa_fwd_bf16_kernel.  The softmax sets each row's
+// reference max from tile 0 and raises it only when a tile's max exceeds it
+// by more than kRescaleThreshold powers of two; that check comes first in a
+// tile, and the rescale runs between two stretches of tile steps (see the
+// loop below), not inside them.
 template <int D, int BC, int WAVES, bool CAUSAL>
 __global__ __launch_bounds__(64 * WAVES, D <= 128 ? 2 : 1) void fa_fwd_bf16_ring_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -832,14 +837,35 @@ __global__ __launch_bounds__(64 * WAVES, D <= 128 ? 2 : 1) void fa_fwd_bf16_ring
   __syncthreads();
   f32x16 s_a[C::KB], s_b[C::KB];
   float mt_a = 0.0f, mt_b = 0.0f;
+  // S(0) and the reference max from it (masked): every row that sees any key
+  // sees key 0, so only rows that see nothing keep -inf.
+  const auto mask_tile = [&](f32x16 (&s)[C::KB], int k0) {
+    const int lim = (CAUSAL ? min(my_q + kshift, Sk - 1) : (Sk - 1)) - k0 - hh * 8;
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kb * 32 + (r >> 3) * 16 + (r & 7);
+        s[kb][r] = key > lim ? -INFINITY : s[kb][r];
+      }
+  };
   if (wave_ntiles > 0) {
     qk_tile<C>(s_a, kb0, qf, k_off);
+    if ((CAUSAL && (BC - 1 > qw0 + kshift)) || (BC > Sk)) mask_tile(s_a, 0);
     mt_a = row_max<C>(s_a, hh);
+    m_run = mt_a;
   }
 
+  // Step j.  When the row's reference max has to move for tile j, the step
+  // leaves at once, having done nothing but mask S(j), with the tile's max in
+  // mt_move, and returns false; the caller rescales and runs step j again.
+  // (The rescale sits outside the loops of steps: inside them the compiler
+  // would keep a copy of the O accumulator in the vector registers at every
+  // step.)
+  float mt_move = 0.0f;
   auto step = [&](const int j, const lds_u8* k_next, lds_u8* k_load, const lds_u8* v_cur,
-                  lds_u8* v_load, f32x16 (&s_in)[C::KB], f32x16 (&s_out)[C::KB],
-                  float& mt_in, float& mt_out) {
+                  lds_u8* v_load, f32x16 (&s_in)[C::KB], f32x16 (&s_out)[C::KB], float& mt_in,
+                  float& mt_out) -> bool {
     // Sources of this step's copies (a valid tile even past the end, so that
     // every step issues the same number of copies).
     const char* kbase;
@@ -853,25 +879,12 @@ __global__ __launch_bounds__(64 * WAVES, D <= 128 ? 2 : 1) void fa_fwd_bf16_ring
       const int k0 = j * BC;
       float mt = mt_in;
       if ((CAUSAL && (k0 + BC - 1 > qw0 + kshift)) || (k0 + BC > Sk)) {
-        const int lim = (CAUSAL ? min(my_q + kshift, Sk - 1) : (Sk - 1)) - k0 - hh * 8;
-#pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kb * 32 + (r >> 3) * 16 + (r & 7);
-            s_in[kb][r] = key > lim ? -INFINITY : s_in[kb][r];
-          }
+        mask_tile(s_in, k0);
         mt = row_max<C>(s_in, hh);
       }
       if (__any((mt - m_run) * c > kRescaleThreshold)) {
-        const float m_new = fmaxf(m_run, mt);
-        const float alpha = m_new == m_run ? 1.0f : fast_exp2((m_run - m_new) * c);
-        m_run = m_new;
-        l_exact *= alpha;
-        l_round0 *= alpha;
-        l_round1 *= alpha;
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) acc[db] *= alpha;
+        mt_move = mt;
+        return false;
       }
       const float mc = m_run == -INFINITY ? 0.0f : m_run * c;
 
@@ -949,19 +962,66 @@ __global__ __launch_bounds__(64 * WAVES, D <= 128 ? 2 : 1) void fa_fwd_bf16_ring
     // this wave's LDS reads are done.
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * NL));
     plain_barrier();
+    return true;
   };
   // Unrolled by four (ring position and S parity static); the remaining
   // tiles run after the loop so that the back edge always follows step 3.
+  // Step j with the buffers of ring position j mod 4 (static, as is the S
+  // parity, in each call below).
+#define FA_RING_STEP(J, POS)                                                       \
+  ((POS) == 0   ? step(J, kb1, kb3, vb0, vb2, s_a, s_b, mt_a, mt_b)               \
+   : (POS) == 1 ? step(J, kb2, kb0, vb1, vb3, s_b, s_a, mt_b, mt_a)               \
+   : (POS) == 2 ? step(J, kb3, kb1, vb2, vb0, s_a, s_b, mt_a, mt_b)               \
+                : step(J, kb0, kb2, vb3, vb1, s_b, s_a, mt_b, mt_a))
+  // Stretches of steps, each until the last tile or until step j needs a
+  // higher reference (need: step j has not run), then the rescale.
   int j = 0;
-  for (; j + 3 < ntiles; j += 4) {
-    step(j, kb1, kb3, vb0, vb2, s_a, s_b, mt_a, mt_b);
-    step(j + 1, kb2, kb0, vb1, vb3, s_b, s_a, mt_b, mt_a);
-    step(j + 2, kb3, kb1, vb2, vb0, s_a, s_b, mt_a, mt_b);
-    step(j + 3, kb0, kb2, vb3, vb1, s_b, s_a, mt_b, mt_a);
+  for (;;) {
+    bool need = false;
+    // up to the next multiple of four, then groups of four
+    switch (j & 3) {
+      case 1:
+        if (j < ntiles) {
+          if (!FA_RING_STEP(j, 1)) { need = true; break; }
+          ++j;
+        }
+        [[fallthrough]];
+      case 2:
+        if (j < ntiles) {
+          if (!FA_RING_STEP(j, 2)) { need = true; break; }
+          ++j;
+        }
+        [[fallthrough]];
+      case 3:
+        if (j < ntiles) {
+          if (!FA_RING_STEP(j, 3)) { need = true; break; }
+          ++j;
+        }
+        [[fallthrough]];
+      default:
+        break;
+    }
+    if (!need) {
+      for (; j < ntiles; j += 4) {
+        if (!FA_RING_STEP(j, 0)) { need = true; break; }
+        if (j + 1 < ntiles && !FA_RING_STEP(j + 1, 1)) { j += 1; need = true; break; }
+        if (j + 2 < ntiles && !FA_RING_STEP(j + 2, 2)) { j += 2; need = true; break; }
+        if (j + 3 < ntiles && !FA_RING_STEP(j + 3, 3)) { j += 3; need = true; break; }
+      }
+    }
+    if (!need) break;
+    // Raise the reference to the masked max of tile j and rescale what was
+    // accumulated over tiles 0 .. j-1; step j then runs with it.
+    const float m_new = fmaxf(m_run, mt_move);
+    const float alpha = m_new == m_run ? 1.0f : fast_exp2((m_run - m_new) * c);
+    m_run = m_new;
+    l_exact *= alpha;
+    l_round0 *= alpha;
+    l_round1 *= alpha;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) acc[db] *= alpha;
   }
-  if (j < ntiles) step(j, kb1, kb3, vb0, vb2, s_a, s_b, mt_a, mt_b);
-  if (j + 1 < ntiles) step(j + 1, kb2, kb0, vb1, vb3, s_b, s_a, mt_b, mt_a);
-  if (j + 2 < ntiles) step(j + 2, kb3, kb1, vb2, vb0, s_a, s_b, mt_a, mt_b);
+#undef FA_RING_STEP
   __builtin_amdgcn_s_waitcnt(0);
 
   const float l_round = l_round0 + l_round1;

@@ -246,6 +246,22 @@ def test_stress_rows_large_scores():
         check(o, lse, o_ref, l_ref, torch.bfloat16, f"stress x32 causal={causal}")
 
 
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_reference_max_raised_many_times(D):
+    # keys scaled up along the sequence (x1 to x31): each row's largest score
+    # keeps growing from tile to tile, far past any threshold for moving the
+    # row's reference max, so the rescale runs several times per row
+    B, H, S = 1, 2, 600
+    q, k, v = wl.make_qkv(B, H, S, D, torch.bfloat16, seed=12)
+    ramp = (1.0 + torch.arange(S, dtype=torch.float32) / 20.0).view(1, 1, S, 1)
+    k = (k.float() * ramp).to(torch.bfloat16)
+    scale = float(torch.tensor(1 / math.sqrt(D), dtype=torch.float32))
+    for causal in (False, True):
+        o, lse = run(q, k, v, causal, scale)
+        o_ref, l_ref = orc.attention_reference(q, k, v, causal, scale)
+        check(o, lse, o_ref, l_ref, torch.bfloat16, f"ramp D={D} causal={causal}")
+
+
 # ---------------------------------------------------------------------------
 # Hygiene: every output written, nothing outside written, deterministic,
 # concurrent streams, host-side rejection of bad pointers
