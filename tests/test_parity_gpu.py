@@ -289,6 +289,29 @@ def test_poisoned_outputs_and_guard_bands(dt):
         assert (lbuf[:pad] == 7).all() and (lbuf[-pad:] == 7).all()
 
 
+@pytest.mark.parametrize("name", ["c4_bf16_causal_1x32x16384x128",
+                                  "c5_bf16_causal_2x8x8192x256_stress"])
+def test_full_size_outputs_all_written(name):
+    # the launch shapes bench.py times, on outputs poisoned with NaN and
+    # guarded by sentinel bands: every O and LSE element is written (finite),
+    # nothing beyond them is
+    w = wl.WORKLOADS[name]
+    q, k, v = (t.cuda() for t in wl.make_inputs(w))
+    n, nl, pad = w.B * w.H * w.S * w.D, w.B * w.H * w.S, 1 << 16
+    obuf = torch.full((n + 2 * pad,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lbuf = torch.full((nl + 2 * pad,), float("nan"), dtype=torch.float32, device="cuda")
+    for buf in (obuf, lbuf):
+        buf[:pad] = 7.0
+        buf[-pad:] = 7.0
+    o = obuf[pad:pad + n].view(w.B, w.H, w.S, w.D)
+    lse = lbuf[pad:pad + nl].view(w.B, w.H, w.S)
+    fa.forward(q, k, v, causal=True, scale=w.scale, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
+    assert bool((obuf[:pad] == 7).all()) and bool((obuf[-pad:] == 7).all())
+    assert bool((lbuf[:pad] == 7).all()) and bool((lbuf[-pad:] == 7).all())
+
+
 def test_deterministic():
     q, k, v = (t.cuda() for t in wl.make_qkv(2, 4, 777, 128, torch.bfloat16, seed=31))
     for causal in (False, True):
