@@ -304,6 +304,37 @@ __device__ __forceinline__ void qk_tile(f32x16 (&s)[C::KB], const lds_u8* Ks,
   }
 }
 
+// K tile stored as two planes, one per half of the head dimension (the
+// head-dim split copy of the pipelining study; D = 128, 64-key tiles): plane
+// h holds dims [64h, 64h + 64) of the tile's rows, 128 bytes per row, with the
+// 16-byte chunks of row r swizzled by (r / 2) mod 8 (a 16-lane pass of 16-byte
+// reads then meets each bank once).
+__device__ __forceinline__ int planar_kswz(int r) { return (r >> 1) & 7; }
+
+// Asynchronous copy of plane h of a K tile (D = 128, BC = 64): 8 pieces of
+// 1 KiB, piece n = rows 8n .. 8n+7; share `part` of COPY_WAVES issues pieces
+// part * per .. part * per + per - 1.  Rows past the sequence end are clamped
+// to the last row (finite data whose keys are masked).
+template <class C>
+__device__ __forceinline__ void copy_k_plane(const uint16_t* __restrict__ head_src, lds_u8* dst,
+                                             int k0, int S, int part, int lane, int h) {
+  static_assert(C::D == 128 && C::BC == 64, "planar K tiles: D = 128, 64-key tiles");
+  constexpr int per = 8 / C::COPY_WAVES;  // pieces of a plane per copy wave
+  const uint64_t b64 = (uint64_t)(head_src + (size_t)k0 * C::D);
+  const uint32_t b_lo = __builtin_amdgcn_readfirstlane((uint32_t)b64);
+  const uint32_t b_hi = __builtin_amdgcn_readfirstlane((uint32_t)(b64 >> 32));
+  const char* base = (const char*)(((uint64_t)b_hi << 32) | b_lo);
+#pragma unroll
+  for (int u = 0; u < per; ++u) {
+    const int n = part * per + u;
+    const int r = 8 * n + (lane >> 3);
+    const int cc = (lane & 7) ^ planar_kswz(r);
+    const int src_row = min(r, S - 1 - k0);
+    lds_dma<16>(base, (uint32_t)(src_row * C::ROW_BYTES + h * 128 + cc * 16),
+                dst + h * 8192 + n * 1024);
+  }
+}
+
 // Row max of a tile's raw scores for the lane's query (both lane halves).
 template <class C>
 __device__ __forceinline__ float row_max(const f32x16 (&s)[C::KB], int hh) {

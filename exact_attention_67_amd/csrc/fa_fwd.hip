@@ -79,6 +79,9 @@ constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 
 enum PipeMode : int {
   kPipeOverlap = 0,     // a tile is copied during the step before it is read; two buffers each
   kPipeNoPrefetch = 1,  // each step copies the tiles it reads, waits for them, then computes
+  kPipeKSplit = 2,      // as kPipeNoPrefetch, with K copied in two head-dim halves: the
+                        // products over dims 0-63 start once the first half has landed
+                        // (D = 128; other head dimensions run kPipeNoPrefetch)
   kPipeRing3 = 3,       // three buffers each; a tile is copied two steps before it is read
   kPipeRing4 = 4,       // four buffers each; a tile is copied three steps before it is read
   kPipeMfmaOnly = 5,    // no copies, no exponentials, no weight check: the products and
@@ -88,7 +91,7 @@ template <int PIPE>
 struct PipeCfg {
   static constexpr int R = PIPE == kPipeRing3 ? 3 : PIPE == kPipeRing4 ? 4 : 2;  // buffers each
   static constexpr int U = R == 3 ? 6 : R;  // steps per unrolled group: buffer slots and S parity
-  static constexpr bool kPrefetch = PIPE != kPipeNoPrefetch;
+  static constexpr bool kPrefetch = PIPE != kPipeNoPrefetch && PIPE != kPipeKSplit;
   static constexpr bool kCopies = PIPE != kPipeMfmaOnly;
   static constexpr bool kSoftmax = PIPE != kPipeMfmaOnly;
 };
@@ -96,8 +99,8 @@ struct PipeCfg {
 #define FA_PIPE 0
 #endif
 constexpr int kPipe = FA_PIPE;
-static_assert(kPipe == kPipeOverlap || kPipe == kPipeNoPrefetch || kPipe == kPipeRing3 ||
-                  kPipe == kPipeRing4 || kPipe == kPipeMfmaOnly,
+static_assert(kPipe == kPipeOverlap || kPipe == kPipeNoPrefetch || kPipe == kPipeKSplit ||
+                  kPipe == kPipeRing3 || kPipe == kPipeRing4 || kPipe == kPipeMfmaOnly,
               "FA_PIPE");
 
 // sched_group_barrier with a compile-time count; nothing when the count is 0.
@@ -245,7 +248,12 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fa_fwd_bf16_kernel(
   // K(0) now; step t copies K(t+1) and V(t-1).
   const auto copy_k = [&](int u, lds_u8* dst) { copy_tile<C, false>(Kh, dst, u * BC, Sk, cw, lane, cl); };
   const auto copy_v = [&](int u, lds_u8* dst) { copy_tile<C, true>(Vh, dst, u * BC, Sk, cw, lane, cl); };
-  if constexpr (PC::kCopies) {
+  if constexpr (PIPE == kPipeKSplit) {
+    if (copier && ntiles > 0) {
+      copy_k_plane<C>(Kh, kslot(I0{}), 0, Sk, cw, lane, 0);
+      copy_k_plane<C>(Kh, kslot(I0{}), 0, Sk, cw, lane, 1);
+    }
+  } else if constexpr (PC::kCopies) {
     if (copier && ntiles > 0) {
       copy_k(0, kslot(I0{}));
       if constexpr (PC::kPrefetch) {
@@ -405,6 +413,25 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fa_fwd_bf16_kernel(
     for (int pc = 0; pc < C::PCH; ++pc) pf[pc] = weights(s, pc, mc, rs);
   };
 
+  // Planar K (kPipeKSplit): the lane's chunk of products ch and ch + 4 (dims
+  // 16 ch + 8 hh .. +8 in planes 0 and 1) for ch = 0..3.
+  int kp_off[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) kp_off[b] = pm * 128 + (((2 * b + hh) ^ planar_kswz(pm)) << 4);
+  // products over dims [64 h, 64 h + 64) of S(tile in ks) into s (the first
+  // half starts the accumulation)
+  const auto qk_half = [&](f32x16 (&s)[C::KB], const lds_u8* ks, auto half_tag) {
+    constexpr int h = decltype(half_tag)::value;
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const bf16x8 kf = *(const lds_bf16x8*)(ks + h * 8192 + kb * 4096 + kp_off[b]);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[4 * h + b],
+                                                        h == 0 && b == 0 ? f32x16{} : s[kb], 0, 0, 0);
+      }
+  };
+
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   // S tiles in two named buffers used alternately (no copy between tiles).
@@ -412,7 +439,12 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fa_fwd_bf16_kernel(
   if (wave_ntiles > 0) {
     // S(0) and the reference max from it: every row that sees any key sees
     // key 0, so only rows that see nothing keep -inf.
-    qk_tile<C>(s_a, kslot(I0{}), qf, k_off);
+    if constexpr (PIPE == kPipeKSplit) {
+      qk_half(s_a, kslot(I0{}), I0{});
+      qk_half(s_a, kslot(I0{}), I1{});
+    } else {
+      qk_tile<C>(s_a, kslot(I0{}), qf, k_off);
+    }
     if (needs_mask(0)) apply_mask(s_a, 0);
     m_run = row_max<C>(s_a, hh);
   }
@@ -429,11 +461,69 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fa_fwd_bf16_kernel(
   // Every path gives the weights and S buffers defined values, so that their
   // previous contents are not kept alive across a step.  The step's position
   // in a group of U steps (PH = t mod U) names its buffers.
-  constexpr int kFirst = 0, kFull = 1, kTail = 2;
   const auto pick = [](auto first_tag, auto& a, auto& b) -> auto& {
     if constexpr (decltype(first_tag)::value) return a;
     else return b;
   };
+  if constexpr (PIPE == kPipeKSplit) {
+    // Step t: copy V(t-1), then K(t+1) in its two head-dim planes; wait for V
+    // and the first plane; P*V of t-1, the weights of t and the products of
+    // S(t+1) over dims 0-63; wait for the second plane; the products over
+    // dims 64-127.  (Unpinned code: a study of the copy split, not of the
+    // schedule.)
+    const auto ks_step = [&](auto ph_tag, const int t) {
+      constexpr int PH = decltype(ph_tag)::value;
+      lds_u8* k_next = kslot(std::integral_constant<int, PH + 1>{});
+      const lds_u8* v_prev = vslot(std::integral_constant<int, PH + 1>{});
+      const std::integral_constant<bool, PH % 2 == 0> even{};
+      f32x16(&s_in)[C::KB] = pick(even, s_a, s_b);
+      f32x16(&s_out)[C::KB] = pick(even, s_b, s_a);
+      const bool k_copy = t + 1 < ntiles;
+      if (copier) {
+        if (t >= 1 && t - 1 < ntiles) copy_v(t - 1, vslot(std::integral_constant<int, PH + 1>{}));
+        if (k_copy) {
+          copy_k_plane<C>(Kh, k_next, (t + 1) * BC, Sk, cw, lane, 0);
+          copy_k_plane<C>(Kh, k_next, (t + 1) * BC, Sk, cw, lane, 1);
+        }
+      }
+      // V and plane 0 have landed, for every wave (plane 1 may be in flight)
+      if (k_copy) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(8 / C::COPY_WAVES));
+      else __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      const bool do_sm = t < wave_ntiles;
+      if (t >= 1 && do_sm && needs_mask(t * BC)) apply_mask(s_in, t * BC);
+      const float mc = ref_mc();
+      float rs = 0.0f;
+      if (t >= 1 && t - 1 < wave_ntiles) {
+        weight_sums();
+#pragma unroll
+        for (int pc = 0; pc < C::PCH; ++pc) pv_chunk(v_prev, pc);
+      }
+#pragma unroll
+      for (int pc = 0; pc < C::PCH; ++pc) pf[pc] = do_sm ? weights(s_in, pc, mc, rs) : bf16x8{};
+      const bool s_next = t + 1 < wave_ntiles;
+      if (s_next) qk_half(s_out, k_next, I0{});
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (s_next) {
+        qk_half(s_out, k_next, I1{});
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb) s_out[kb] = f32x16{};
+      }
+      if (do_sm) {
+        if (__any(!(rs <= kRowSumLimit))) raise_reference(s_in, rs);
+        l_exact += rs;
+      }
+    };
+    int t = 0;
+    for (; t + 1 <= ntiles; t += 2) {
+      ks_step(I0{}, t);
+      ks_step(I1{}, t + 1);
+    }
+    if (t <= ntiles) ks_step(I0{}, t);
+  } else {
+  constexpr int kFirst = 0, kFull = 1, kTail = 2;
   auto step = [&](auto kind_tag, auto ph_tag, const int t) {
     constexpr int KIND = decltype(kind_tag)::value;
     constexpr int PH = decltype(ph_tag)::value;
@@ -642,6 +732,8 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fa_fwd_bf16_kernel(
     // no copy into this workgroup's LDS is still in flight when it ends
     __builtin_amdgcn_s_waitcnt(0);
   }
+
+  }  // pipeline modes
 
   const float le = l_exact + swap_halves(l_exact, hh);
   const float lr = MFMA_SUM ? l_mfma[0] : l_round + swap_halves(l_round, hh);
@@ -1290,6 +1382,8 @@ int run_bf16(const void* q, const void* k, const void* v, void* o, float* lse, i
   const uint16_t* K = static_cast<const uint16_t*>(k);
   const uint16_t* V = static_cast<const uint16_t*>(v);
   uint16_t* Out = static_cast<uint16_t*>(o);
+  // the head-dim split copy exists for D = 128 only
+  constexpr int P = kPipe == kPipeKSplit && D != 128 ? kPipeNoPrefetch : kPipe;
   if constexpr (D == 256) {
     if (causal)
       return launch(fa_fwd_bf16_ring_kernel<D, BC, WAVES, true>, cfg.grid, 64 * WAVES, stream, Q,
@@ -1298,9 +1392,9 @@ int run_bf16(const void* q, const void* k, const void* v, void* o, float* lse, i
                   V, Out, lse, Sq, Sk, cfg.nq, p.bh_total, p.group_heads, p.c);
   } else {
     if (causal)
-      return launch(fa_fwd_bf16_kernel<D, BC, WAVES, true, kMfmaSum, kPipe>, cfg.grid, 64 * WAVES, stream,
+      return launch(fa_fwd_bf16_kernel<D, BC, WAVES, true, kMfmaSum, P>, cfg.grid, 64 * WAVES, stream,
                     Q, K, V, Out, lse, Sq, Sk, cfg.nq, p.bh_total, p.group_heads, p.c);
-    return launch(fa_fwd_bf16_kernel<D, BC, WAVES, false, kMfmaSum, kPipe>, cfg.grid, 64 * WAVES, stream,
+    return launch(fa_fwd_bf16_kernel<D, BC, WAVES, false, kMfmaSum, P>, cfg.grid, 64 * WAVES, stream,
                   Q, K, V, Out, lse, Sq, Sk, cfg.nq, p.bh_total, p.group_heads, p.c);
   }
 }

@@ -1,13 +1,16 @@
 """The tile-pipeline study builds (libfa_mi355x_pipe_<name>.so: the bf16
-forward with K/V tiles copied without prefetch, or two or three steps ahead
-into three or four buffers each) compute the same attention as the library.
+forward with K/V tiles copied without prefetch, without prefetch and K in two
+head-dim halves (the products over the first half start once it has landed),
+or two or three steps ahead into three or four buffers each) compute the same
+attention as the library.
 
 Each is checked against the float64 oracle, to the tolerances of
 test_parity_gpu.py, on ragged shapes that run the 128-row and the 256-row
 workgroups and enough key tiles to pass through every unrolled step group,
 and bit for bit against the library on a longer causal problem (the three
 builds run the same arithmetic in the same order; only the copies and waits
-differ).  The products-only probe (mfma_only) is a timing probe whose results
+differ; the head-dim split sums the same products in the same order).  The
+products-only probe (mfma_only) is a timing probe whose results
 are void: it is only checked to run."""
 
 import math
@@ -23,7 +26,7 @@ from tests.test_parity_gpu import check
 
 pytestmark = pytest.mark.gpu
 
-CORRECT = ("noprefetch", "ring3", "ring4")
+CORRECT = ("noprefetch", "ksplit", "ring3", "ring4")
 
 # B, H, S, D, causal (rows per workgroup follow from the library's plan)
 SHAPES = [
