@@ -22,8 +22,8 @@
 //    out with one key per lane (the forward's S^T = K Q^T with the roles of
 //    queries and keys exchanged), so P and dS are per-lane columns; dV += P^T dO
 //    and dK += dS^T q read dO and q with the transposing LDS read.  q and dO
-//    are each needed both row-wise and transposed, so each query tile is
-//    copied into LDS twice, once per swizzle.  Its registers (about 480 per
+//    are each needed both row-wise and transposed; each query tile is copied
+//    once, in a swizzle that serves both reads, into three stages.  Its registers (about 480 per
 //    lane) allow one wavefront per SIMD, so each wave overlaps its own work:
 //    S and dP of the next query tile are computed while the weights and dS
 //    of the current one form.  At D = 256 the query tiles are 32 rows and
@@ -110,277 +110,6 @@ __device__ __forceinline__ void store_col(uint16_t* __restrict__ out_row, const 
     }
 }
 
-// Per-lane byte offsets for the row reads (A operand of qk_tile, rows read in
-// the permuted order) and the transposing reads of a tile; as in the forward.
-template <class C>
-__device__ __forceinline__ void operand_offsets(int lane, int (&k_off)[C::NKOFF],
-                                                int (&v_off)[C::NVOFF]) {
-  const int m = lane & 31, hh = lane >> 5;
-  const int pm = key_perm(m);
-  const int ksw = kswz<C>(pm);
-#pragma unroll
-  for (int b = 0; b < C::NKOFF; ++b) k_off[b] = pm * C::ROW_BYTES + (((2 * b + hh) ^ ksw) << 4);
-  const int g = lane >> 4, j4 = (lane >> 2) & 3, t4 = lane & 3;
-  const int vx = 2 * (g & 1) + (t4 >> 1);
-  const int vsw = vswz<C>(hh * 8 + j4);
-  const int v_row = (hh * 8 + j4) * C::ROW_BYTES + (t4 & 1) * 8;
-#pragma unroll
-  for (int d4 = 0; d4 < C::NVOFF; ++d4) v_off[d4] = v_row + (((4 * d4 + vx) ^ vsw) << 4);
-}
-
-// Fragments of one row (lane's row `row` of a [S, D] matrix) as the B operand
-// of qk_tile: lane holds X[row][ch*16 + hh*8 .. +8]; zero past the end.
-template <class C>
-__device__ __forceinline__ void row_fragments(bf16x8 (&f)[C::KCH], const uint16_t* __restrict__ X,
-                                              int row, int S, int hh) {
-#pragma unroll
-  for (int ch = 0; ch < C::KCH; ++ch) {
-    u32x4 raw = u32x4{0u, 0u, 0u, 0u};
-    if (row < S) raw = *reinterpret_cast<const u32x4*>(X + (size_t)row * C::D + ch * 16 + hh * 8);
-    f[ch] = __builtin_bit_cast(bf16x8, raw);
-  }
-}
-
-// One 32-row block of S = X * frag^T (rows of the tile X, read in the
-// permuted order, against the lane's own fragment): s = X[kb*32 + perm(m)] . frag.
-template <class C>
-__device__ __forceinline__ void qk_block(f32x16& s, const lds_u8* X, const bf16x8 (&f)[C::KCH],
-                                         const int (&k_off)[C::NKOFF], int kb) {
-#pragma unroll
-  for (int ch = 0; ch < C::KCH; ++ch) {
-    const bf16x8 xf = *(const lds_bf16x8*)(X + kb * 32 * C::ROW_BYTES + (ch / C::NKOFF) * 256 +
-                                           k_off[ch % C::NKOFF]);
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf, f[ch], ch == 0 ? f32x16{} : s, 0, 0, 0);
-  }
-}
-
-// acc[hb] += A^T * bf for the 16 contraction rows of chunk pc (A read
-// transposed from a V-swizzled tile), for NB 32-wide head-dim blocks starting
-// at block part * NB.
-template <class C, int NB>
-__device__ __forceinline__ void tr_chunk(f32x16 (&acc)[NB], const lds_u8* tile,
-                                         const bf16x8& bf, const int (&v_off)[C::NVOFF], int pc,
-                                         int part) {
-  static_assert(NB % C::NVOFF == 0, "a head-dim part spans whole offset groups");
-  const lds_u8* t = tile + pc * 16 * C::ROW_BYTES + part * (NB / C::NVOFF) * 256;
-#pragma unroll
-  for (int db = 0; db < NB; ++db) {
-    const lds_u8* p = t + (db / C::NVOFF) * 256 + v_off[db % C::NVOFF];
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * C::ROW_BYTES));
-    const bf16x8 af =
-        __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc[db], 0, 0, 0);
-  }
-}
-
-// ----------------------------------------------------------------------------
-// dK, dV: one workgroup per (128 keys, head, batch, head-dim part)
-// ----------------------------------------------------------------------------
-// Query tiles t stream through LDS.  Step t computes, on the matrix cores,
-// S(t+1) and dP(t+1) for the next tile while the weights P(t) and dS(t) form,
-// then dV += P(t)^T dO(t) and dK += dS(t)^T q(t).  The row-layout copies of q
-// and dO (read by S and dP) therefore run one tile ahead of the transposed
-// copies (read by the dV and dK products) and of LSE and Delta.
-template <int D, int BQ, int NP, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void fa_bwd_dkdv_kernel(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-    const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-    const float* __restrict__ LSE, const float* __restrict__ Delta, uint16_t* __restrict__ dK,
-    uint16_t* __restrict__ dV, int S, int nk, int bh_total, int group_heads, float c,
-    float scale) {
-  using C = BfCfg<D, BQ, 4>;  // query tiles of BQ rows; 4 waves of 32 keys
-  // The head dimensions of dK and dV are split into NP parts, one workgroup
-  // each (NP = 2 at D = 256, where two full accumulators do not fit beside
-  // the K and V fragments); every part computes the full S and dP.
-  constexpr int NB = C::DB / NP;  // 32-wide head-dim blocks of this part
-  // Query tile in two layouts (row reads: K swizzle; transposed reads: V
-  // swizzle) for q and dO, two stages; each a separately named array.
-  __shared__ __attribute__((aligned(1024))) uint8_t qr0_raw[C::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t qr1_raw[C::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t qt0_raw[C::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t qt1_raw[C::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t dr0_raw[C::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t dr1_raw[C::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t dt0_raw[C::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t dt1_raw[C::TILE_BYTES];
-  __shared__ __attribute__((aligned(256))) uint8_t ls0_raw[256];
-  __shared__ __attribute__((aligned(256))) uint8_t ls1_raw[256];
-  __shared__ __attribute__((aligned(256))) uint8_t de0_raw[256];
-  __shared__ __attribute__((aligned(256))) uint8_t de1_raw[256];
-  lds_u8* qr0 = (lds_u8*)qr0_raw;
-  lds_u8* qr1 = (lds_u8*)qr1_raw;
-  lds_u8* qt0 = (lds_u8*)qt0_raw;
-  lds_u8* qt1 = (lds_u8*)qt1_raw;
-  lds_u8* dr0 = (lds_u8*)dr0_raw;
-  lds_u8* dr1 = (lds_u8*)dr1_raw;
-  lds_u8* dt0 = (lds_u8*)dt0_raw;
-  lds_u8* dt1 = (lds_u8*)dt1_raw;
-  lds_u8* ls0 = (lds_u8*)ls0_raw;
-  lds_u8* ls1 = (lds_u8*)ls1_raw;
-  lds_u8* de0 = (lds_u8*)de0_raw;
-  lds_u8* de1 = (lds_u8*)de1_raw;
-
-  // Heaviest key blocks (the first ones, seen by most query tiles) first.
-  int bh, kt;
-  const int L = xcd_logical_index(blockIdx.x, nk * bh_total * NP);  // parts adjacent: same XCD
-  const int part = L % NP;
-  decode_tile<CAUSAL>(L / NP, nk, bh_total, group_heads, bh, kt);
-  if (CAUSAL) kt = nk - 1 - kt;
-
-  const size_t head = (size_t)bh * (size_t)S * D;
-  const uint16_t* Qh = Q + head;
-  const uint16_t* Kh = K + head;
-  const uint16_t* Vh = V + head;
-  const uint16_t* dOh = dO + head;
-  const float* LSEh = LSE + (size_t)bh * S;
-  const float* Dh = Delta + (size_t)bh * S;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int m = lane & 31;
-  const int hh = lane >> 5;
-  const int k0 = kt * 128;
-  const int kw0 = k0 + wave * kRowsPerWave;
-  const int my_k = kw0 + m;
-
-  // Query tiles this workgroup visits: causal -- those with a query >= k0.
-  // A wave takes part in tile t when some query of the tile sees one of its
-  // keys (with the causal mask this holds for every tile after its first).
-  const int nt = (S + BQ - 1) / BQ;
-  const int t_first = CAUSAL ? k0 / BQ : 0;
-  auto live = [&](int t) { return kw0 < S && (!CAUSAL || t * BQ + BQ - 1 >= kw0); };
-
-  int qoff[C::LOADS_PER_WAVE], qrow[C::LOADS_PER_WAVE];
-  int toff[C::LOADS_PER_WAVE], trow[C::LOADS_PER_WAVE];
-  tile_offsets<C, false>(qoff, qrow, wave, lane);
-  tile_offsets<C, true>(toff, trow, wave, lane);
-  auto copy_rows = [&](int t, lds_u8* qr, lds_u8* dr) {
-    const int q0 = t * BQ;
-    issue_tile<C>(Qh, qr, q0, S, wave, qoff, qrow);
-    issue_tile<C>(dOh, dr, q0, S, wave, qoff, qrow);
-  };
-  auto copy_cols = [&](int t, lds_u8* qt, lds_u8* dt, lds_u8* ls, lds_u8* de) {
-    const int q0 = t * BQ;
-    issue_tile<C>(Qh, qt, q0, S, wave, toff, trow);
-    issue_tile<C>(dOh, dt, q0, S, wave, toff, trow);
-    if (wave == 0) issue_rowvec(LSEh, ls, q0, S, lane);
-    if (wave == 1) issue_rowvec(Dh, de, q0, S, lane);
-  };
-
-  bf16x8 kf[C::KCH], vf[C::KCH];
-  row_fragments<C>(kf, Kh, my_k, S, hh);
-  row_fragments<C>(vf, Vh, my_k, S, hh);
-  int k_off[C::NKOFF], v_off[C::NVOFF];
-  operand_offsets<C>(lane, k_off, v_off);
-
-  f32x16 dk_acc[NB], dv_acc[NB];
-#pragma unroll
-  for (int db = 0; db < NB; ++db) {
-    dk_acc[db] = f32x16{};
-    dv_acc[db] = f32x16{};
-  }
-
-  if (t_first < nt) {
-    copy_rows(t_first, qr0, dr0);
-    copy_cols(t_first, qt0, dt0, ls0, de0);
-  }
-  if (t_first + 1 < nt) copy_rows(t_first + 1, qr1, dr1);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  // S and dP tiles in two named sets used alternately.
-  f32x16 s_a[C::KB], dp_a[C::KB], s_b[C::KB], dp_b[C::KB];
-  if (t_first < nt && live(t_first)) {
-#pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb) {
-      qk_block<C>(s_a[kb], qr0, kf, k_off, kb);
-      qk_block<C>(dp_a[kb], dr0, vf, k_off, kb);
-    }
-  }
-  __syncthreads();  // every wave is done with the rows of the first tile
-
-  // Step t: start the row copies of tile t+2 and the transposed copies (and
-  // LSE, Delta) of tile t+1; S(t+1), dP(t+1) into s_out, dp_out while P(t),
-  // dS(t) form from s_in, dp_in; then the dV and dK products of tile t.
-  auto step = [&](const int t, const lds_u8* qr_n, const lds_u8* dr_n, lds_u8* qr_l,
-                  lds_u8* dr_l, const lds_u8* qt, const lds_u8* dt, const lds_u8* ls,
-                  const lds_u8* de, lds_u8* qt_l, lds_u8* dt_l, lds_u8* ls_l, lds_u8* de_l,
-                  f32x16 (&s_in)[C::KB], f32x16 (&dp_in)[C::KB], f32x16 (&s_out)[C::KB],
-                  f32x16 (&dp_out)[C::KB]) {
-    if (t + 2 < nt) copy_rows(t + 2, qr_l, dr_l);
-    if (t + 1 < nt) copy_cols(t + 1, qt_l, dt_l, ls_l, de_l);
-    const int q0 = t * BQ;
-    if (live(t)) {
-      // ---- mask (diagonal and tail tiles): excluded scores -> -inf ------------
-      if ((CAUSAL && q0 < kw0 + 31) || (q0 + BQ > S)) {
-#pragma unroll
-        for (int qb = 0; qb < C::KB; ++qb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            // register r of block qb holds query row 32*qb + 16*(r/8) + 8*hh + r%8
-            const int q = q0 + 32 * qb + 16 * (r >> 3) + 8 * hh + (r & 7);
-            if (q >= S || (CAUSAL && my_k > q)) s_in[qb][r] = -INFINITY;
-          }
-      }
-      bf16x8 pq[C::PCH], dsq[C::PCH];
-      // weights and dS of the 16-query chunk pc (registers 8*half .. +7 of block qb)
-      auto chunk = [&](int qb, int half) {
-        const int rb = 32 * qb + 16 * half + 8 * hh;
-        const int pc = 2 * qb + half;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int r = 8 * half + e;
-          const float lse2 = reinterpret_cast<const lds_f32*>(ls)[rb + e] * kLog2e;
-          const float del = reinterpret_cast<const lds_f32*>(de)[rb + e];
-          const float p = fast_exp2(fmaf(s_in[qb][r], c, -lse2));
-          pq[pc][e] = (__bf16)p;
-          dsq[pc][e] = (__bf16)(p * (dp_in[qb][r] - del));
-        }
-      };
-      // The products of a 16-query chunk follow the chunk's weights, and
-      // S(t+1), dP(t+1) are split around them, so the matrix cores always
-      // have independent work while the weights form.  The compiler's
-      // MFMA/LDS interleave strategy 1 orders the region (measured: 3-6 %
-      // faster than its default order; pinning the order with scheduling
-      // group barriers, as the forward does, was 7 % slower).
-#pragma unroll
-      for (int qb = 0; qb < C::KB; ++qb) {
-        qk_block<C>(s_out[qb], qr_n, kf, k_off, qb);
-        qk_block<C>(dp_out[qb], dr_n, vf, k_off, qb);
-        chunk(qb, 0);
-        chunk(qb, 1);
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          tr_chunk<C, NB>(dv_acc, dt, pq[2 * qb + half], v_off, 2 * qb + half, part);   // dV^T += dO^T P
-          tr_chunk<C, NB>(dk_acc, qt, dsq[2 * qb + half], v_off, 2 * qb + half, part);  // dK^T += q^T dS
-        }
-      }
-      __builtin_amdgcn_iglp_opt(1);
-    } else if (t + 1 < nt && live(t + 1)) {
-      // the wave's first tile is the next one: only S(t+1), dP(t+1)
-#pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb) {
-        qk_block<C>(s_out[kb], qr_n, kf, k_off, kb);
-        qk_block<C>(dp_out[kb], dr_n, vf, k_off, kb);
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-  };
-  int t = t_first;
-  for (; t + 1 < nt; t += 2) {
-    step(t, qr1, dr1, qr0, dr0, qt0, dt0, ls0, de0, qt1, dt1, ls1, de1, s_a, dp_a, s_b, dp_b);
-    step(t + 1, qr0, dr0, qr1, dr1, qt1, dt1, ls1, de1, qt0, dt0, ls0, de0, s_b, dp_b, s_a, dp_a);
-  }
-  if (t < nt)
-    step(t, qr1, dr1, qr0, dr0, qt0, dt0, ls0, de0, qt1, dt1, ls1, de1, s_a, dp_a, s_b, dp_b);
-
-  if (my_k >= S) return;
-  store_col<NB>(dK + head + (size_t)my_k * D + part * NB * 32, dk_acc, scale, hh);
-  store_col<NB>(dV + head + (size_t)my_k * D + part * NB * 32, dv_acc, 1.0f, hh);
-}
-
 // One swizzle for tiles read both row-wise (16 rows of one chunk column per
 // pass) and with the transposing read (4 consecutive rows x 4 chunks per
 // pass), conflict-free for both: a bijection of the 16 rows of a pass onto
@@ -424,6 +153,268 @@ __device__ __forceinline__ void operand_offsets_u(int lane, int (&k_off)[C::NKOF
     v_off[d4] = v_row + (((4 * d4 + vx) ^ vsw) << 4);
     v_hi[d4] = v_row + 4 * C::ROW_BYTES + (((4 * d4 + vx) ^ vsw4) << 4);
   }
+}
+
+// Fragments of one row (lane's row `row` of a [S, D] matrix) as the B operand
+// of qk_tile: lane holds X[row][ch*16 + hh*8 .. +8]; zero past the end.
+template <class C>
+__device__ __forceinline__ void row_fragments(bf16x8 (&f)[C::KCH], const uint16_t* __restrict__ X,
+                                              int row, int S, int hh) {
+#pragma unroll
+  for (int ch = 0; ch < C::KCH; ++ch) {
+    u32x4 raw = u32x4{0u, 0u, 0u, 0u};
+    if (row < S) raw = *reinterpret_cast<const u32x4*>(X + (size_t)row * C::D + ch * 16 + hh * 8);
+    f[ch] = __builtin_bit_cast(bf16x8, raw);
+  }
+}
+
+// One 32-row block of S = X * frag^T (rows of the tile X, read in the
+// permuted order, against the lane's own fragment): s = X[kb*32 + perm(m)] . frag.
+template <class C>
+__device__ __forceinline__ void qk_block(f32x16& s, const lds_u8* X, const bf16x8 (&f)[C::KCH],
+                                         const int (&k_off)[C::NKOFF], int kb) {
+#pragma unroll
+  for (int ch = 0; ch < C::KCH; ++ch) {
+    const bf16x8 xf = *(const lds_bf16x8*)(X + kb * 32 * C::ROW_BYTES + (ch / C::NKOFF) * 256 +
+                                           k_off[ch % C::NKOFF]);
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf, f[ch], ch == 0 ? f32x16{} : s, 0, 0, 0);
+  }
+}
+
+// acc[hb] += A^T * bf for the 16 contraction rows of chunk pc (A read
+// transposed from a tile in the unified swizzle), for NB 32-wide head-dim
+// blocks starting at block part * NB.
+template <class C, int NB>
+__device__ __forceinline__ void tr_chunk(f32x16 (&acc)[NB], const lds_u8* tile,
+                                         const bf16x8& bf, const int (&v_off)[C::NVOFF],
+                                         const int (&v_hi)[C::NVOFF], int pc, int part) {
+  static_assert(NB % C::NVOFF == 0, "a head-dim part spans whole offset groups");
+  const lds_u8* t = tile + pc * 16 * C::ROW_BYTES + part * (NB / C::NVOFF) * 256;
+#pragma unroll
+  for (int db = 0; db < NB; ++db) {
+    const lds_u8* b = t + (db / C::NVOFF) * 256;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b + v_off[db % C::NVOFF]));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b + v_hi[db % C::NVOFF]));
+    const bf16x8 af =
+        __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc[db], 0, 0, 0);
+  }
+}
+
+// ----------------------------------------------------------------------------
+// dK, dV: one workgroup per (128 keys, head, batch, head-dim part)
+// ----------------------------------------------------------------------------
+// Query tiles t stream through LDS.  Step t computes, on the matrix cores,
+// S(t+1) and dP(t+1) for the next tile while the weights P(t) and dS(t) form,
+// then dV += P(t)^T dO(t) and dK += dS(t)^T q(t).  Each q and dO tile is
+// stored once, in the swizzle that serves both its row reads (S, dP, one step
+// before its weights) and its transposed reads (dV, dK), in three stages:
+// during step t tile t+1 is read by rows, tile t transposed, and tile t+2
+// lands in the third.  LSE and Delta of tile t+1 land during step t.
+template <int D, int BQ, int NP, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void fa_bwd_dkdv_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+    const float* __restrict__ LSE, const float* __restrict__ Delta, uint16_t* __restrict__ dK,
+    uint16_t* __restrict__ dV, int S, int nk, int bh_total, int group_heads, float c,
+    float scale) {
+  using C = BfCfg<D, BQ, 4>;  // query tiles of BQ rows; 4 waves of 32 keys
+  // The head dimensions of dK and dV are split into NP parts, one workgroup
+  // each (NP = 2 at D = 256, where two full accumulators do not fit beside
+  // the K and V fragments); every part computes the full S and dP.
+  constexpr int NB = C::DB / NP;  // 32-wide head-dim blocks of this part
+  // Three stages of q and dO tiles, each a separately named array: the
+  // compiler then sees that a step's copies and its operand reads touch
+  // different arrays, and waits for the copies only where asked (the end of
+  // the step), not before the step's first read.
+  __shared__ __attribute__((aligned(1024))) uint8_t q0_raw[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t q1_raw[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t q2_raw[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t d0_raw[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t d1_raw[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t d2_raw[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(256))) uint8_t ls0_raw[256];
+  __shared__ __attribute__((aligned(256))) uint8_t ls1_raw[256];
+  __shared__ __attribute__((aligned(256))) uint8_t de0_raw[256];
+  __shared__ __attribute__((aligned(256))) uint8_t de1_raw[256];
+  lds_u8* q0s = (lds_u8*)q0_raw;
+  lds_u8* q1s = (lds_u8*)q1_raw;
+  lds_u8* q2s = (lds_u8*)q2_raw;
+  lds_u8* d0s = (lds_u8*)d0_raw;
+  lds_u8* d1s = (lds_u8*)d1_raw;
+  lds_u8* d2s = (lds_u8*)d2_raw;
+  lds_u8* ls0 = (lds_u8*)ls0_raw;
+  lds_u8* ls1 = (lds_u8*)ls1_raw;
+  lds_u8* de0 = (lds_u8*)de0_raw;
+  lds_u8* de1 = (lds_u8*)de1_raw;
+
+  // Heaviest key blocks (the first ones, seen by most query tiles) first.
+  int bh, kt;
+  const int L = xcd_logical_index(blockIdx.x, nk * bh_total * NP);  // parts adjacent: same XCD
+  const int part = L % NP;
+  decode_tile<CAUSAL>(L / NP, nk, bh_total, group_heads, bh, kt);
+  if (CAUSAL) kt = nk - 1 - kt;
+
+  const size_t head = (size_t)bh * (size_t)S * D;
+  const uint16_t* Qh = Q + head;
+  const uint16_t* Kh = K + head;
+  const uint16_t* Vh = V + head;
+  const uint16_t* dOh = dO + head;
+  const float* LSEh = LSE + (size_t)bh * S;
+  const float* Dh = Delta + (size_t)bh * S;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int m = lane & 31;
+  const int hh = lane >> 5;
+  const int k0 = kt * 128;
+  const int kw0 = k0 + wave * kRowsPerWave;
+  const int my_k = kw0 + m;
+
+  // Query tiles this workgroup visits: causal -- those with a query >= k0.
+  // A wave takes part in tile t when some query of the tile sees one of its
+  // keys (with the causal mask this holds for every tile after its first).
+  const int nt = (S + BQ - 1) / BQ;
+  const int t_first = CAUSAL ? k0 / BQ : 0;
+  auto live = [&](int t) { return kw0 < S && (!CAUSAL || t * BQ + BQ - 1 >= kw0); };
+
+  int off[C::LOADS_PER_WAVE], row[C::LOADS_PER_WAVE];
+  tile_offsets_u<C>(off, row, wave, lane);
+  auto copy_tile = [&](int t, lds_u8* qd, lds_u8* dd) {
+    const int q0 = t * BQ;
+    issue_tile<C>(Qh, qd, q0, S, wave, off, row);
+    issue_tile<C>(dOh, dd, q0, S, wave, off, row);
+  };
+  auto copy_vecs = [&](int t, lds_u8* ls, lds_u8* de) {
+    const int q0 = t * BQ;
+    if (wave == 0) issue_rowvec(LSEh, ls, q0, S, lane);
+    if (wave == 1) issue_rowvec(Dh, de, q0, S, lane);
+  };
+
+  bf16x8 kf[C::KCH], vf[C::KCH];
+  row_fragments<C>(kf, Kh, my_k, S, hh);
+  row_fragments<C>(vf, Vh, my_k, S, hh);
+  int k_off[C::NKOFF], v_off[C::NVOFF], v_hi[C::NVOFF];
+  operand_offsets_u<C>(lane, k_off, v_off, v_hi);
+
+  f32x16 dk_acc[NB], dv_acc[NB];
+#pragma unroll
+  for (int db = 0; db < NB; ++db) {
+    dk_acc[db] = f32x16{};
+    dv_acc[db] = f32x16{};
+  }
+
+  if (t_first < nt) {
+    copy_tile(t_first, q0s, d0s);
+    copy_vecs(t_first, ls0, de0);
+  }
+  if (t_first + 1 < nt) copy_tile(t_first + 1, q1s, d1s);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  // S and dP tiles in two named sets used alternately.
+  f32x16 s_a[C::KB], dp_a[C::KB], s_b[C::KB], dp_b[C::KB];
+  if (t_first < nt && live(t_first)) {
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb) {
+      qk_block<C>(s_a[kb], q0s, kf, k_off, kb);
+      qk_block<C>(dp_a[kb], d0s, vf, k_off, kb);
+    }
+  }
+  // (step t_first copies into the third slot and the second LSE/Delta
+  // buffers, which nothing has read yet: no barrier needed here)
+
+  // Step t: q and dO of tile t in qt, dt (read transposed), of tile t+1 in
+  // qr_n, dr_n (read by rows); tile t+2 lands in q_l, d_l, and LSE, Delta of
+  // tile t+1 in ls_l, de_l.  S(t+1), dP(t+1) go to s_out, dp_out while P(t),
+  // dS(t) form from s_in, dp_in; then the dV and dK products of tile t.
+  auto step = [&](const int t, const lds_u8* qt, const lds_u8* dt, const lds_u8* qr_n,
+                  const lds_u8* dr_n, lds_u8* q_l, lds_u8* d_l, const lds_u8* ls,
+                  const lds_u8* de, lds_u8* ls_l, lds_u8* de_l, f32x16 (&s_in)[C::KB],
+                  f32x16 (&dp_in)[C::KB], f32x16 (&s_out)[C::KB], f32x16 (&dp_out)[C::KB]) {
+    if (t + 2 < nt) copy_tile(t + 2, q_l, d_l);
+    if (t + 1 < nt) copy_vecs(t + 1, ls_l, de_l);
+    const int q0 = t * BQ;
+    if (live(t)) {
+      // ---- mask (diagonal and tail tiles): excluded scores -> -inf ------------
+      if ((CAUSAL && q0 < kw0 + 31) || (q0 + BQ > S)) {
+#pragma unroll
+        for (int qb = 0; qb < C::KB; ++qb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            // register r of block qb holds query row 32*qb + 16*(r/8) + 8*hh + r%8
+            const int q = q0 + 32 * qb + 16 * (r >> 3) + 8 * hh + (r & 7);
+            if (q >= S || (CAUSAL && my_k > q)) s_in[qb][r] = -INFINITY;
+          }
+      }
+      bf16x8 pq[C::PCH], dsq[C::PCH];
+      // weights and dS of the 16-query chunk pc (registers 8*half .. +7 of block qb)
+      auto chunk = [&](int qb, int half) {
+        const int rb = 32 * qb + 16 * half + 8 * hh;
+        const int pc = 2 * qb + half;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int r = 8 * half + e;
+          const float lse2 = reinterpret_cast<const lds_f32*>(ls)[rb + e] * kLog2e;
+          const float del = reinterpret_cast<const lds_f32*>(de)[rb + e];
+          const float p = fast_exp2(fmaf(s_in[qb][r], c, -lse2));
+          pq[pc][e] = (__bf16)p;
+          dsq[pc][e] = (__bf16)(p * (dp_in[qb][r] - del));
+        }
+      };
+      // The products of a 16-query chunk follow the chunk's weights, and
+      // S(t+1), dP(t+1) are split around them, so the matrix cores always
+      // have independent work while the weights form.  The compiler's
+      // MFMA/LDS interleave strategy 1 orders the region (measured: 3-6 %
+      // faster than its default order; pinning the order with scheduling
+      // group barriers, as the forward does, was 7 % slower).
+#pragma unroll
+      for (int qb = 0; qb < C::KB; ++qb) {
+        qk_block<C>(s_out[qb], qr_n, kf, k_off, qb);
+        qk_block<C>(dp_out[qb], dr_n, vf, k_off, qb);
+        chunk(qb, 0);
+        chunk(qb, 1);
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int pc = 2 * qb + half;
+          tr_chunk<C, NB>(dv_acc, dt, pq[pc], v_off, v_hi, pc, part);   // dV^T += dO^T P
+          tr_chunk<C, NB>(dk_acc, qt, dsq[pc], v_off, v_hi, pc, part);  // dK^T += q^T dS
+        }
+      }
+      __builtin_amdgcn_iglp_opt(1);
+    } else if (t + 1 < nt && live(t + 1)) {
+      // the wave's first tile is the next one: only S(t+1), dP(t+1)
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb) {
+        qk_block<C>(s_out[kb], qr_n, kf, k_off, kb);
+        qk_block<C>(dp_out[kb], dr_n, vf, k_off, kb);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+  // Six steps per pass: the three stages rotate, and the S/dP sets and the
+  // LSE/Delta buffers alternate, with every buffer named at compile time.
+  if (t_first < nt) {
+    for (int t = t_first;;) {
+      step(t, q0s, d0s, q1s, d1s, q2s, d2s, ls0, de0, ls1, de1, s_a, dp_a, s_b, dp_b);
+      if (++t >= nt) break;
+      step(t, q1s, d1s, q2s, d2s, q0s, d0s, ls1, de1, ls0, de0, s_b, dp_b, s_a, dp_a);
+      if (++t >= nt) break;
+      step(t, q2s, d2s, q0s, d0s, q1s, d1s, ls0, de0, ls1, de1, s_a, dp_a, s_b, dp_b);
+      if (++t >= nt) break;
+      step(t, q0s, d0s, q1s, d1s, q2s, d2s, ls1, de1, ls0, de0, s_b, dp_b, s_a, dp_a);
+      if (++t >= nt) break;
+      step(t, q1s, d1s, q2s, d2s, q0s, d0s, ls0, de0, ls1, de1, s_a, dp_a, s_b, dp_b);
+      if (++t >= nt) break;
+      step(t, q2s, d2s, q0s, d0s, q1s, d1s, ls1, de1, ls0, de0, s_b, dp_b, s_a, dp_a);
+      if (++t >= nt) break;
+    }
+  }
+
+  if (my_k >= S) return;
+  store_col<NB>(dK + head + (size_t)my_k * D + part * NB * 32, dk_acc, scale, hh);
+  store_col<NB>(dV + head + (size_t)my_k * D + part * NB * 32, dv_acc, 1.0f, hh);
 }
 
 // acc[db] += A^T * bf, A read transposed from a tile in the unified swizzle.
