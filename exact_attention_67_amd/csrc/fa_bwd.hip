@@ -437,6 +437,247 @@ __device__ __forceinline__ void tr_product_u(f32x16 (&acc)[C::DB], const lds_u8*
 }
 
 // ----------------------------------------------------------------------------
+// dK, dV with wave pairs (D = 64, 128): one workgroup of 8 wavefronts per
+// (block of 128 keys, head, batch)
+// ----------------------------------------------------------------------------
+// Waves w and w + 4 run on the same SIMD and own the same 32 keys; they split
+// the work on each 64-query tile.  The P wave computes S = q K^T, the weights
+// P and dV += P^T dO, and leaves P (bf16, the operand of its dV product) in
+// LDS.  The dS wave computes dP = dO V^T, and one tile later, with that P,
+// dS = P (dP - Delta) and dK += dS^T q.  Each wave holds about half the state
+// of a wave doing both (its fragments, its accumulators, one score tile), so
+// two of them fit on a SIMD and keep its matrix core busy while the other
+// waits on LDS or forms weights.
+//
+// Tiles: q(t), LSE(t), Delta(t) in stage (t - t_first) mod 3, dO(t) in stage
+// (t - t_first) mod 2 (nothing reads dO(t-1) during step t).  Step t copies
+// tile t+1 into the next stages; the P wave reads q(t) by rows and dO(t)
+// transposed, the dS wave dO(t) by rows and q(t-1) transposed.  P(t) goes to
+// exchange buffer (t - t_first) mod 2.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_pair_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+    const float* __restrict__ LSE, const float* __restrict__ Delta, uint16_t* __restrict__ dK,
+    uint16_t* __restrict__ dV, int S, int nk, int bh_total, int group_heads, float c,
+    float scale) {
+  constexpr int BQ = 64;
+  using C = BfCfg<D, BQ, 4>;        // tile geometry; each role copies its tensor in 4 parts
+  constexpr int XB = C::PCH * 1024;  // P of one pair and tile: PCH chunks x 64 lanes x 16 B
+  static_assert(C::KB == 2 && C::PCH == 4, "64-query tiles");
+  __shared__ __attribute__((aligned(1024))) uint8_t q0_raw[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t q1_raw[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t q2_raw[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t d0_raw[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t d1_raw[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t x0_raw[4 * XB];
+  __shared__ __attribute__((aligned(1024))) uint8_t x1_raw[4 * XB];
+  __shared__ __attribute__((aligned(256))) uint8_t l0_raw[256];
+  __shared__ __attribute__((aligned(256))) uint8_t l1_raw[256];
+  __shared__ __attribute__((aligned(256))) uint8_t l2_raw[256];
+  __shared__ __attribute__((aligned(256))) uint8_t e0_raw[256];
+  __shared__ __attribute__((aligned(256))) uint8_t e1_raw[256];
+  __shared__ __attribute__((aligned(256))) uint8_t e2_raw[256];
+  lds_u8* q0s = (lds_u8*)q0_raw;
+  lds_u8* q1s = (lds_u8*)q1_raw;
+  lds_u8* q2s = (lds_u8*)q2_raw;
+  lds_u8* d0s = (lds_u8*)d0_raw;
+  lds_u8* d1s = (lds_u8*)d1_raw;
+  lds_u8* x0s = (lds_u8*)x0_raw;
+  lds_u8* x1s = (lds_u8*)x1_raw;
+  lds_u8* l0s = (lds_u8*)l0_raw;
+  lds_u8* l1s = (lds_u8*)l1_raw;
+  lds_u8* l2s = (lds_u8*)l2_raw;
+  lds_u8* e0s = (lds_u8*)e0_raw;
+  lds_u8* e1s = (lds_u8*)e1_raw;
+  lds_u8* e2s = (lds_u8*)e2_raw;
+
+  // Heaviest key blocks (the first ones, seen by most query tiles) first.
+  int bh, kt;
+  decode_tile<CAUSAL>(xcd_logical_index(blockIdx.x, nk * bh_total), nk, bh_total, group_heads,
+                      bh, kt);
+  if (CAUSAL) kt = nk - 1 - kt;
+
+  const size_t head = (size_t)bh * (size_t)S * D;
+  const uint16_t* Qh = Q + head;
+  const uint16_t* dOh = dO + head;
+  const float* LSEh = LSE + (size_t)bh * S;
+  const float* Dh = Delta + (size_t)bh * S;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pr = wave & 3;        // pair: keys kw0 .. kw0 + 31
+  const bool p_wave = wave < 4;   // role (wave-uniform)
+  const int m = lane & 31;
+  const int hh = lane >> 5;
+  const int k0 = kt * 128;
+  const int kw0 = k0 + pr * kRowsPerWave;
+  const int my_k = kw0 + m;
+
+  // Query tiles this workgroup visits: causal -- those with a query >= k0.
+  // A pair takes part in tile t when some query of the tile sees one of its
+  // keys (with the causal mask this holds for every tile after its first).
+  const int nt = (S + BQ - 1) / BQ;
+  const int t_first = CAUSAL ? k0 / BQ : 0;
+  auto live = [&](int t) { return kw0 < S && (!CAUSAL || t * BQ + BQ - 1 >= kw0); };
+
+  // Copies: the P waves copy q, the dS waves dO (each wave a quarter), wave 0
+  // LSE and wave 4 Delta.
+  // (offsets recomputed at each copy rather than held through the loop)
+  auto copy_tile = [&](int t, lds_u8* qd, lds_u8* dd, lds_u8* ld, lds_u8* ed) {
+    const int q0 = t * BQ;
+    int off[C::LOADS_PER_WAVE], row[C::LOADS_PER_WAVE];
+    tile_offsets_u<C>(off, row, pr, lane);
+    if (p_wave) {
+      issue_tile<C>(Qh, qd, q0, S, pr, off, row);
+      if (wave == 0) issue_rowvec(LSEh, ld, q0, S, lane);
+    } else {
+      issue_tile<C>(dOh, dd, q0, S, pr, off, row);
+      if (wave == 4) issue_rowvec(Dh, ed, q0, S, lane);
+    }
+  };
+
+  // The lane's key fragment: K for the P wave (S), V for the dS wave (dP).
+  bf16x8 kf[C::KCH];
+  row_fragments<C>(kf, (p_wave ? K : V) + head, my_k, S, hh);
+  int k_off[C::NKOFF], v_off[C::NVOFF], v_hi[C::NVOFF];
+  operand_offsets_u<C>(lane, k_off, v_off, v_hi);
+
+  f32x16 acc[C::DB];  // dV (P wave) or dK (dS wave), transposed
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
+
+  // P wave, tile t: S from q(t), mask, weights, P to the exchange buffer,
+  // dV += P^T dO(t).
+  auto p_step = [&](const int t, const lds_u8* qs, const lds_u8* dsn, const lds_u8* ls,
+                    lds_u8* xs) {
+    if (!live(t)) return;
+    f32x16 s[C::KB];
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb) qk_block<C>(s[kb], qs, kf, k_off, kb);
+    const int q0 = t * BQ;
+    if ((CAUSAL && q0 < kw0 + 31) || (q0 + BQ > S)) {
+#pragma unroll
+      for (int qb = 0; qb < C::KB; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          // register r of block qb holds query row 32*qb + 16*(r/8) + 8*hh + r%8
+          const int q = q0 + 32 * qb + 16 * (r >> 3) + 8 * hh + (r & 7);
+          if (q >= S || (CAUSAL && my_k > q)) s[qb][r] = -INFINITY;
+        }
+    }
+    lds_u8* xw = xs + pr * XB + lane * 16;
+#pragma unroll
+    for (int pc = 0; pc < C::PCH; ++pc) {
+      const int qb = pc >> 1, half = pc & 1;
+      const int rb = 32 * qb + 16 * half + 8 * hh;
+      bf16x8 pq;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float lse2 = reinterpret_cast<const lds_f32*>(ls)[rb + e] * kLog2e;
+        pq[e] = (__bf16)fast_exp2(fmaf(s[qb][8 * half + e], c, -lse2));
+      }
+      *(lds_bf16x8*)(xw + pc * 1024) = pq;
+      tr_chunk<C, C::DB>(acc, dsn, pq, v_off, v_hi, pc, 0);  // dV^T += dO^T P
+    }
+  };
+  // dS wave, step t: dP(t) from dO(t) into dp_out (d_dp); dS(t-1) from
+  // P(t-1) (xs), dP(t-1) (dp_in) and Delta(t-1), dK += dS^T q(t-1) (d_ds).
+  auto d_dp = [&](const int t, const lds_u8* dsr, f32x16 (&dp_out)[C::KB]) {
+    if (!live(t)) return;
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb) qk_block<C>(dp_out[kb], dsr, kf, k_off, kb);
+  };
+  auto d_ds = [&](const int tp, const lds_u8* qprev, const lds_u8* eprev, const lds_u8* xs,
+                  const f32x16 (&dp_in)[C::KB]) {
+    if (!live(tp)) return;
+    const lds_u8* xr = xs + pr * XB + lane * 16;
+#pragma unroll
+    for (int pc = 0; pc < C::PCH; ++pc) {
+      const int qb = pc >> 1, half = pc & 1;
+      const int rb = 32 * qb + 16 * half + 8 * hh;
+      const bf16x8 pq = *(const lds_bf16x8*)(xr + pc * 1024);
+      bf16x8 dsq;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float del = reinterpret_cast<const lds_f32*>(eprev)[rb + e];
+        dsq[e] = (__bf16)((float)pq[e] * (dp_in[qb][8 * half + e] - del));
+      }
+      tr_chunk<C, C::DB>(acc, qprev, dsq, v_off, v_hi, pc, 0);  // dK^T += q^T dS
+    }
+  };
+  auto d_step = [&](const int t, const lds_u8* dsr, const lds_u8* qprev, const lds_u8* eprev,
+                    const lds_u8* xs, f32x16 (&dp_out)[C::KB], const f32x16 (&dp_in)[C::KB]) {
+    if (t < nt) d_dp(t, dsr, dp_out);
+    if (t > t_first) d_ds(t - 1, qprev, eprev, xs, dp_in);
+  };
+
+  if (t_first < nt) copy_tile(t_first, q0s, d0s, l0s, e0s);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  // Each role runs its own loop (so neither holds the other's registers);
+  // both take one barrier per step, the same steps, so the workgroup's
+  // barriers stay matched.  Six steps per pass (three q stages; two dO
+  // stages, exchange buffers and dP sets), every buffer named at compile
+  // time.  Step: copy tile t+1 into the next stages, the role's work, wait
+  // for the copies, barrier.
+#define FA_PAIR_COPY(QN, DN, LN, EN) \
+  if (t + 1 < nt) copy_tile(t + 1, QN, DN, LN, EN);
+#define FA_PAIR_END                    \
+  __builtin_amdgcn_s_waitcnt(0);       \
+  __syncthreads();
+  if (p_wave) {
+    if (t_first < nt) {
+      for (int t = t_first;;) {
+        FA_PAIR_COPY(q1s, d1s, l1s, e1s) p_step(t, q0s, d0s, l0s, x0s); FA_PAIR_END
+        if (++t >= nt) break;
+        FA_PAIR_COPY(q2s, d0s, l2s, e2s) p_step(t, q1s, d1s, l1s, x1s); FA_PAIR_END
+        if (++t >= nt) break;
+        FA_PAIR_COPY(q0s, d1s, l0s, e0s) p_step(t, q2s, d0s, l2s, x0s); FA_PAIR_END
+        if (++t >= nt) break;
+        FA_PAIR_COPY(q1s, d0s, l1s, e1s) p_step(t, q0s, d1s, l0s, x1s); FA_PAIR_END
+        if (++t >= nt) break;
+        FA_PAIR_COPY(q2s, d1s, l2s, e2s) p_step(t, q1s, d0s, l1s, x0s); FA_PAIR_END
+        if (++t >= nt) break;
+        FA_PAIR_COPY(q0s, d0s, l0s, e0s) p_step(t, q2s, d1s, l2s, x1s); FA_PAIR_END
+        if (++t >= nt) break;
+      }
+    }
+    if (my_k < S) store_col<C::DB>(dV + head + (size_t)my_k * D, acc, 1.0f, hh);
+    return;
+  }
+  // dS wave: one step more than the P wave (t = nt: the final tile's dS and
+  // dK only, with no copy and no barrier).
+#define FA_PAIR_DEND            \
+  if (t < nt) {                 \
+    FA_PAIR_END                 \
+  }
+  f32x16 dp_a[C::KB], dp_b[C::KB];  // dP of the current and the previous tile
+  if (t_first < nt) {
+    for (int t = t_first;;) {
+      FA_PAIR_COPY(q1s, d1s, l1s, e1s) d_step(t, d0s, q2s, e2s, x1s, dp_a, dp_b); FA_PAIR_DEND
+      if (++t > nt) break;
+      FA_PAIR_COPY(q2s, d0s, l2s, e2s) d_step(t, d1s, q0s, e0s, x0s, dp_b, dp_a); FA_PAIR_DEND
+      if (++t > nt) break;
+      FA_PAIR_COPY(q0s, d1s, l0s, e0s) d_step(t, d0s, q1s, e1s, x1s, dp_a, dp_b); FA_PAIR_DEND
+      if (++t > nt) break;
+      FA_PAIR_COPY(q1s, d0s, l1s, e1s) d_step(t, d1s, q2s, e2s, x0s, dp_b, dp_a); FA_PAIR_DEND
+      if (++t > nt) break;
+      FA_PAIR_COPY(q2s, d1s, l2s, e2s) d_step(t, d0s, q0s, e0s, x1s, dp_a, dp_b); FA_PAIR_DEND
+      if (++t > nt) break;
+      FA_PAIR_COPY(q0s, d0s, l0s, e0s) d_step(t, d1s, q1s, e1s, x0s, dp_b, dp_a); FA_PAIR_DEND
+      if (++t > nt) break;
+    }
+  }
+#undef FA_PAIR_DEND
+#undef FA_PAIR_COPY
+#undef FA_PAIR_END
+  if (my_k < S) store_col<C::DB>(dK + head + (size_t)my_k * D, acc, scale, hh);
+}
+
+// ----------------------------------------------------------------------------
 // dQ: one workgroup per (256 queries, head, batch)
 // ----------------------------------------------------------------------------
 template <int D, int BC, int WAVES, bool CAUSAL>
@@ -581,7 +822,16 @@ int run_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint1
   constexpr int NP = D == 256 ? 2 : 1;  // head-dim parts of dK/dV
   const int nk = (S + 127) / 128;
   const unsigned grid = (unsigned)nk * (unsigned)bh * NP;
-  if (causal)
+  if constexpr (D != 256) {
+    if (causal)
+      st = launch_k(fa_bwd_dkdv_pair_kernel<D, true>, grid, 512, s, q, k, v, dout,
+                    (const float*)lse, (const float*)delta, dk, dv, S, nk, bh, group_heads, c,
+                    scale);
+    else
+      st = launch_k(fa_bwd_dkdv_pair_kernel<D, false>, grid, 512, s, q, k, v, dout,
+                    (const float*)lse, (const float*)delta, dk, dv, S, nk, bh, group_heads, c,
+                    scale);
+  } else if (causal)
     st = launch_k(fa_bwd_dkdv_kernel<D, BT, NP, true>, grid, 256, s, q, k, v, dout,
                   (const float*)lse, (const float*)delta, dk, dv, S, nk, bh, group_heads, c, scale);
   else
