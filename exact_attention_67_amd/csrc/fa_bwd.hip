@@ -156,15 +156,16 @@ __device__ __forceinline__ void operand_offsets_u(int lane, int (&k_off)[C::NKOF
 }
 
 // Fragments of one row (lane's row `row` of a [S, D] matrix) as the B operand
-// of qk_tile: lane holds X[row][ch*16 + hh*8 .. +8]; zero past the end.
+// of qk_tile: lane holds X[row][ch*16 + hh*8 .. +8], its sign bits XORed with
+// `flip` (negated for a negative scale); zero past the end.
 template <class C>
 __device__ __forceinline__ void row_fragments(bf16x8 (&f)[C::KCH], const uint16_t* __restrict__ X,
-                                              int row, int S, int hh) {
+                                              int row, int S, int hh, uint32_t flip = 0u) {
 #pragma unroll
   for (int ch = 0; ch < C::KCH; ++ch) {
     u32x4 raw = u32x4{0u, 0u, 0u, 0u};
     if (row < S) raw = *reinterpret_cast<const u32x4*>(X + (size_t)row * C::D + ch * 16 + hh * 8);
-    f[ch] = __builtin_bit_cast(bf16x8, raw);
+    f[ch] = __builtin_bit_cast(bf16x8, raw ^ flip);
   }
 }
 
@@ -293,8 +294,10 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dkdv_kernel(
   };
 
   bf16x8 kf[C::KCH], vf[C::KCH];
-  row_fragments<C>(kf, Kh, my_k, S, hh);
+  // negative scale: S from -K with |c| (see kZeroScaleC); dK uses q as it is
+  row_fragments<C>(kf, Kh, my_k, S, hh, sign_flip_mask(c));
   row_fragments<C>(vf, Vh, my_k, S, hh);
+  c = fabsf(c);
   int k_off[C::NKOFF], v_off[C::NVOFF], v_hi[C::NVOFF];
   operand_offsets_u<C>(lane, k_off, v_off, v_hi);
 
@@ -540,7 +543,10 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_pair_kernel(
 
   // The lane's key fragment: K for the P wave (S), V for the dS wave (dP).
   bf16x8 kf[C::KCH];
-  row_fragments<C>(kf, (p_wave ? K : V) + head, my_k, S, hh);
+  // (negative scale: the P wave's S from -K with |c|, see kZeroScaleC; dK
+  // uses q as it is)
+  row_fragments<C>(kf, (p_wave ? K : V) + head, my_k, S, hh, p_wave ? sign_flip_mask(c) : 0u);
+  c = fabsf(c);
   int k_off[C::NKOFF], v_off[C::NVOFF], v_hi[C::NVOFF];
   operand_offsets_u<C>(lane, k_off, v_off, v_hi);
 
@@ -735,8 +741,10 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 2 : 1) void fa_bwd_dq_kern
   };
 
   bf16x8 qf[C::KCH], df[C::KCH];
-  row_fragments<C>(qf, Qh, my_q, S, hh);
+  // negative scale: S^T from -q with |c| (see kZeroScaleC); dq uses K as it is
+  row_fragments<C>(qf, Qh, my_q, S, hh, sign_flip_mask(c));
   row_fragments<C>(df, dOh, my_q, S, hh);
+  c = fabsf(c);
   int k_off[C::NKOFF], v_off[C::NVOFF], v_hi[C::NVOFF];
   operand_offsets_u<C>(lane, k_off, v_off, v_hi);
   const float lse2 = my_q < S ? LSE[(size_t)bh * S + my_q] * kLog2e : 0.0f;
@@ -810,7 +818,7 @@ int run_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint1
             const uint16_t* dout, const float* lse, uint16_t* dq, uint16_t* dk, uint16_t* dv,
             float* delta, int bh, int S, bool causal, float scale, hipStream_t s) {
   const int64_t rows = (int64_t)bh * S;
-  const float c = scale * kLog2e;
+  const float c = scale == 0.0f ? kZeroScaleC : scale * kLog2e;  // sign: see kZeroScaleC
   const int group_heads = bh >= 8 ? bh / 8 : 1;
   int st = launch_k(fa_bwd_delta_kernel<D>, (unsigned)((rows * (D / 8) + 255) / 256), 256, s,
                     o, dout, delta, rows);
@@ -859,7 +867,7 @@ int validate_bwd(const void* q, const void* k, const void* v, const void* o, con
   if (B < 1 || H < 1 || S < 1) return FA_ERR_SHAPE;
   if (D != 64 && D != 128 && D != 256) return FA_ERR_HEADDIM;
   if (causal != 0 && causal != 1) return FA_ERR_CAUSAL;
-  if (!(scale > 0.0f) || !isfinite(scale)) return FA_ERR_SCALE;
+  if (!isfinite(scale)) return FA_ERR_SCALE;
   const int64_t bh = (int64_t)B * H;
   const int64_t nk = ((int64_t)S + 127) / 128;
   if (bh > INT32_MAX || (int64_t)S * D > INT32_MAX || 2 * nk * bh > INT32_MAX ||

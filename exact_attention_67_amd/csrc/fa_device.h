@@ -26,6 +26,16 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
 
+// The kernels take the score multiplier as c = scale * log2(e) and work with
+// |c|.  A negative c stands for a negative scale: the kernel negates one
+// operand of the score product (the sign bits of a register fragment, an
+// exact operation), so scale * q.k = |scale| * (-q).k.  A zero scale arrives
+// as kZeroScaleC: every visible key then gets the weight exp2(s * c - m * c)
+// = 1 exactly (the argument is below 2^-24 for any finite score), and masked
+// keys (score -inf) keep weight 0; -inf * 0 would give NaN instead.
+constexpr float kZeroScaleC = 0x1p-100f;
+__device__ __forceinline__ uint32_t sign_flip_mask(float c) { return c < 0.0f ? 0x80008000u : 0u; }
+
 constexpr int kRowsPerWave = 32;  // query (or key) rows per wavefront
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

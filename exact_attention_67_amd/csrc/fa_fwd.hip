@@ -171,6 +171,9 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fa_fwd_bf16_kernel(
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
     int Sq, int Sk, int nq, int bh_total, int group_heads, float c) {
   using C = BfCfg<D, BC, WAVES>;
+  // negative scale: S from -Q with |c| (see kZeroScaleC)
+  const uint32_t qflip = sign_flip_mask(c);
+  c = fabsf(c);
   using PC = PipeCfg<PIPE>;
   constexpr int R = PC::R, U = PC::U;
   // Separate buffers (R for K, R for V) rather than one array indexed by tile
@@ -276,7 +279,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fa_fwd_bf16_kernel(
   for (int ch = 0; ch < C::KCH; ++ch) {
     u32x4 raw = u32x4{0u, 0u, 0u, 0u};
     if (my_q < Sq) raw = *reinterpret_cast<const u32x4*>(Qh + (size_t)my_q * D + ch * 16 + hh * 8);
-    qf[ch] = __builtin_bit_cast(bf16x8, raw);
+    qf[ch] = __builtin_bit_cast(bf16x8, raw ^ qflip);
   }
 
   // Per-lane byte offsets of the operand reads inside a buffer.
@@ -819,6 +822,9 @@ __global__ __launch_bounds__(64 * WAVES, D <= 128 ? 2 : 1) void fa_fwd_bf16_ring
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
     int Sq, int Sk, int nq, int bh_total, int group_heads, float c) {
   using C = BfCfg<D, BC, WAVES>;
+  // negative scale: S from -Q with |c| (see kZeroScaleC)
+  const uint32_t qflip = sign_flip_mask(c);
+  c = fabsf(c);
   // Every wave copies its share (wave w fills bytes [w, w+1) * NL KiB of a
   // buffer): the copy split must cover exactly the waves of the workgroup.
   static_assert(C::COPY_WAVES == WAVES, "ring kernel: every wave issues tile copies");
@@ -903,7 +909,7 @@ __global__ __launch_bounds__(64 * WAVES, D <= 128 ? 2 : 1) void fa_fwd_bf16_ring
   for (int ch = 0; ch < C::KCH; ++ch) {
     u32x4 raw = u32x4{0u, 0u, 0u, 0u};
     if (my_q < Sq) raw = *reinterpret_cast<const u32x4*>(Qh + (size_t)my_q * D + ch * 16 + hh * 8);
-    qf[ch] = __builtin_bit_cast(bf16x8, raw);
+    qf[ch] = __builtin_bit_cast(bf16x8, raw ^ qflip);
   }
 
   const int pm = key_perm(m);
@@ -1161,6 +1167,9 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_f32_kernel(
     float* __restrict__ O, float* __restrict__ LSE, int S, int nq, int bh_total,
     int group_heads, float c) {
   using C = F32Cfg<D>;
+  // negative scale: S from -Q with |c| (see kZeroScaleC)
+  const float qsign = c < 0.0f ? -1.0f : 1.0f;
+  c = fabsf(c);
   constexpr int BC = C::BC;
   __shared__ float smem[C::ELEMS];
   float* Ks = smem;
@@ -1190,7 +1199,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_f32_kernel(
   // B operand of S^T = K * Q^T: lane holds Q[my_q][2*ch + hh].
   float qf[D / 2];
 #pragma unroll
-  for (int ch = 0; ch < D / 2; ++ch) qf[ch] = (my_q < S) ? Qh[(size_t)my_q * D + 2 * ch + hh] : 0.0f;
+  for (int ch = 0; ch < D / 2; ++ch) qf[ch] = (my_q < S) ? qsign * Qh[(size_t)my_q * D + 2 * ch + hh] : 0.0f;
 
   f32x16 acc[C::DB];
 #pragma unroll
@@ -1318,7 +1327,7 @@ int validate(const void* q, const void* k, const void* v, const void* o, const f
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   const int st = validate_shape(B, H, Sq, Sk, D, causal, elem);
   if (st != FA_OK) return st;
-  if (!(scale > 0.0f) || !isfinite(scale)) return FA_ERR_SCALE;
+  if (!isfinite(scale)) return FA_ERR_SCALE;
   const int64_t bh = (int64_t)B * H;
   const uintptr_t a16 = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o;
   if ((a16 & 15u) || ((uintptr_t)lse & 3u)) return FA_ERR_ALIGN;
@@ -1332,7 +1341,7 @@ int validate(const void* q, const void* k, const void* v, const void* o, const f
     return FA_ERR_ALIAS;
   plan->bh_total = (int)bh;
   plan->group_heads = bh >= 8 ? (int)(bh / 8) : 1;
-  plan->c = scale * kLog2e;
+  plan->c = scale == 0.0f ? kZeroScaleC : scale * kLog2e;  // sign: see kZeroScaleC
   return FA_OK;
 }
 
@@ -1577,7 +1586,7 @@ extern "C" const char* fa_status_str(int status) {
     case FA_ERR_NULL: return "a tensor pointer is NULL";
     case FA_ERR_SHAPE: return "a size (B, H, S, Sq, Sk or G) is < 1, or a size overflows";
     case FA_ERR_HEADDIM: return "head dimension must be 64, 128 or 256";
-    case FA_ERR_SCALE: return "scale must be finite and > 0";
+    case FA_ERR_SCALE: return "scale must be finite";
     case FA_ERR_CAUSAL: return "causal must be 0 or 1";
     case FA_ERR_ALIGN: return "q/k/v/o must be 16-byte aligned and lse 4-byte aligned";
     case FA_ERR_ALIAS: return "o or lse overlaps an input or each other";

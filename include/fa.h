@@ -54,7 +54,7 @@ enum fa_status {
     FA_ERR_NULL    = 1, /* a tensor pointer is NULL */
     FA_ERR_SHAPE   = 2, /* B, H, S (Sq, Sk, G) < 1, or a size/offset overflows */
     FA_ERR_HEADDIM = 3, /* D not one of 64, 128, 256 */
-    FA_ERR_SCALE   = 4, /* scale not finite or not > 0 */
+    FA_ERR_SCALE   = 4, /* scale not finite (NaN or +-inf) */
     FA_ERR_CAUSAL  = 5, /* causal not 0 or 1 */
     FA_ERR_ALIGN   = 6, /* q/k/v/o not 16-byte aligned or lse not 4-byte aligned */
     FA_ERR_ALIAS   = 7, /* o or lse overlaps an input or each other */
@@ -75,7 +75,10 @@ enum fa_status {
  *   B, H, S : batch, heads, sequence length (>= 1).
  *   D       : head dimension, one of 64, 128, 256.
  *   causal  : 1 = key j visible to query i iff j <= i; 0 = all keys.
- *   scale   : score multiplier, finite and > 0 (usually 1/sqrt(D)).
+ *   scale   : score multiplier, any finite value (usually 1/sqrt(D)).  A
+ *             negative scale is computed exactly as |scale| on negated q; a
+ *             zero scale gives every visible key the same weight (O = mean of
+ *             the visible v rows, lse = log of their count).
  *   stream  : hipStream_t to enqueue on (NULL = default stream).
  * Arithmetic: bf16 products with float32 accumulation for both contractions;
  * the softmax (running max, exponentials, running sum) is float32; the softmax

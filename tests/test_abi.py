@@ -91,7 +91,7 @@ def test_validation_errors(f32):
         assert call(D=d, f32=f32) == fa.FA_ERR_HEADDIM, d
     for c in (-1, 2, 7):
         assert call(causal=c, f32=f32) == fa.FA_ERR_CAUSAL, c
-    for s in (0.0, -0.125, math.inf, -math.inf, math.nan):
+    for s in (math.inf, -math.inf, math.nan):  # any finite scale is accepted
         assert call(scale=s, f32=f32) == fa.FA_ERR_SCALE, s
     assert call(q=Q + 8, f32=f32) == fa.FA_ERR_ALIGN
     assert call(o=O + 4, f32=f32) == fa.FA_ERR_ALIGN
@@ -179,7 +179,7 @@ def test_bwd_validation_errors():
     for d in (32, 96, 512):
         assert call_bwd(D=d) == fa.FA_ERR_HEADDIM, d
     assert call_bwd(causal=5) == fa.FA_ERR_CAUSAL
-    assert call_bwd(scale=0.0) == fa.FA_ERR_SCALE
+    assert call_bwd(scale=-math.inf) == fa.FA_ERR_SCALE
     assert call_bwd(dk=A * 8 + 8) == fa.FA_ERR_ALIGN
     assert call_bwd(delta=A * 10 + 2) == fa.FA_ERR_ALIGN
     nb = 1 * 2 * 100 * 128 * 2

@@ -343,3 +343,31 @@ def test_default_scale_closed_forms():
     o_default, l_default = orc.attention_reference(q, k, v, True)
     o_eighth, l_eighth = orc.attention_reference(q, k, v, True, 0.125)
     assert torch.equal(o_default, o_eighth) and torch.equal(l_default, l_eighth)
+
+
+def test_zero_scale_closed_form():
+    # scale = 0: every score is 0, so each row's softmax is uniform over its
+    # visible keys: O = mean of those v rows, LSE = log(count).
+    g = torch.Generator().manual_seed(91)
+    B, H, S, D = 1, 2, 9, 8
+    q, k, v = (torch.randn(B, H, S, D, generator=g, dtype=torch.float64) for _ in range(3))
+    for causal in (False, True):
+        o, lse = orc.attention_reference(q, k, v, causal, 0.0)
+        for i in range(S):
+            n = i + 1 if causal else S
+            assert torch.allclose(o[..., i, :], v[..., :n, :].mean(dim=-2), rtol=0, atol=1e-14)
+            assert torch.allclose(lse[..., i], torch.full((B, H), math.log(n), dtype=torch.float64),
+                                  rtol=0, atol=1e-14)
+
+
+def test_negative_scale_is_the_positive_one_on_negated_queries():
+    # scale * q.k = (-scale) * (-q).k: the oracle must use the scale's sign
+    # (a dropped sign, |scale|, fails this for a non-symmetric input).
+    g = torch.Generator().manual_seed(92)
+    q, k, v = (torch.randn(1, 2, 17, 16, generator=g, dtype=torch.float64) for _ in range(3))
+    for causal in (False, True):
+        o1, l1 = orc.attention_reference(q, k, v, causal, -0.3)
+        o2, l2 = orc.attention_reference(-q, k, v, causal, 0.3)
+        o3, _ = orc.attention_reference(q, k, v, causal, 0.3)
+        assert torch.allclose(o1, o2, rtol=0, atol=1e-13) and torch.allclose(l1, l2, rtol=0, atol=1e-13)
+        assert (o1 - o3).abs().max().item() > 1e-3

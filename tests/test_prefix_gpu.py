@@ -212,7 +212,7 @@ def test_bad_arguments_rejected_before_launch():
     q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16, device="cuda")
     k = torch.zeros(1, 1, 16, 64, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(fa.FAError):
-        fa.forward_kv(q, k, k, causal=True, scale=-1.0)
+        fa.forward_kv(q, k, k, causal=True, scale=math.nan)
     with pytest.raises(ValueError):
         fa.forward_kv(q, k[:, :, :, :32].contiguous(), k[:, :, :, :32].contiguous())
     op = torch.zeros(2, 1, 1, 8, 64, dtype=torch.bfloat16, device="cuda")

@@ -50,7 +50,7 @@ def test_fwd_rejections_on_real_buffers(arena, f32):
     _, p = arena
     fn = fa.fa_fwd_f32 if f32 else fa.fa_fwd
     n = 1 * 2 * 128 * 64 * (4 if f32 else 2)
-    for s in (0.0, -0.125, math.inf, -math.inf, math.nan):
+    for s in (math.inf, -math.inf, math.nan):
         assert fwd(fn, p, scale=s) == fa.FA_ERR_SCALE, s
     assert fwd(fn, p, q=p[0] + 8) == fa.FA_ERR_ALIGN
     assert fwd(fn, p, o=p[3] + 4) == fa.FA_ERR_ALIGN
@@ -70,7 +70,7 @@ def test_fwd_kv_rejections_on_real_buffers(arena):
     kbytes = 1 * 2 * 300 * 128 * 2
     qbytes = 1 * 2 * 64 * 128 * 2
     assert call(scale=math.nan) == fa.FA_ERR_SCALE
-    assert call(scale=-1.0) == fa.FA_ERR_SCALE
+    assert call(scale=-math.inf) == fa.FA_ERR_SCALE
     assert call(k=p[1] + 8) == fa.FA_ERR_ALIGN
     assert call(lse=p[4] + 1) == fa.FA_ERR_ALIGN
     assert call(o=p[1] + kbytes - 16) == fa.FA_ERR_ALIAS
@@ -102,7 +102,7 @@ def test_bwd_rejections_on_real_buffers(arena):
         return fa.fa_bwd(*(a[n] for n in names), 1, 2, 100, 128, 1, scale, None)
 
     nb = 1 * 2 * 100 * 128 * 2
-    for s in (0.0, -1.0, math.nan, math.inf):
+    for s in (math.nan, math.inf, -math.inf):
         assert call(scale=s) == fa.FA_ERR_SCALE, s
     assert call(dk=p[7] + 8) == fa.FA_ERR_ALIGN
     assert call(delta=p[9] + 2) == fa.FA_ERR_ALIGN
