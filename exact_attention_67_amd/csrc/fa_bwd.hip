@@ -587,6 +587,9 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_pair_kernel(
       *(lds_bf16x8*)(xw + pc * 1024) = pq;
       tr_chunk<C, C::DB>(acc, dsn, pq, v_off, v_hi, pc, 0);  // dV^T += dO^T P
     }
+    // compiler MFMA/LDS interleave strategy 1 (measured: 1 % faster here, and
+    // 2.5 % slower in the dS wave, which keeps the default order)
+    __builtin_amdgcn_iglp_opt(1);
   };
   // dS wave, step t: dP(t) from dO(t) into dp_out (d_dp); dS(t-1) from
   // P(t-1) (xs), dP(t-1) (dp_in) and Delta(t-1), dK += dS^T q(t-1) (d_ds).
