@@ -13,22 +13,25 @@
 //   dS    = P * (dP - Delta)
 //   dq    = scale * dS k,   dk = scale * dS^T q
 //
-// Three kernels:
+// Three kernels (four templates):
 //  * fa_bwd_delta_kernel: Delta (one row per TPR consecutive lanes).
-//  * fa_bwd_dkdv_kernel: one workgroup of 4 wavefronts per (block of 128 keys,
-//    head, batch); each wave owns 32 keys and keeps their K and V fragments and
-//    dK, dV accumulators in registers, while tiles of queries (q and dO, plus
-//    their LSE and Delta) stream through LDS.  S = q K^T and dP = dO V^T come
-//    out with one key per lane (the forward's S^T = K Q^T with the roles of
-//    queries and keys exchanged), so P and dS are per-lane columns; dV += P^T dO
-//    and dK += dS^T q read dO and q with the transposing LDS read.  q and dO
-//    are each needed both row-wise and transposed; each query tile is copied
-//    once, in a swizzle that serves both reads, into three stages.  Its registers (about 480 per
-//    lane) allow one wavefront per SIMD, so each wave overlaps its own work:
-//    S and dP of the next query tile are computed while the weights and dS
-//    of the current one form.  At D = 256 the query tiles are 32 rows and
-//    the head dimensions of dK and dV are split between two workgroups per
-//    key block (both compute S and dP), so that a part's accumulators fit.
+//  * fa_bwd_dkdv_pair_kernel (D = 64, 128): one workgroup of 8 wavefronts per
+//    (block of 128 keys, head, batch).  Waves w and w + 4 share a SIMD and own
+//    the same 32 keys; the P wave forms S = q K^T, the weights P and dV, and
+//    hands P to the dS wave through LDS, which forms dP = dO V^T, dS and dK
+//    one tile later.  S and dP come out with one key per lane (the forward's
+//    S^T = K Q^T with the roles of queries and keys exchanged), so P and dS
+//    are per-lane columns; dV += P^T dO and dK += dS^T q read dO and q with
+//    the transposing LDS read.  Each query tile of q and dO is copied once,
+//    in a swizzle that serves both the row reads and the transposing reads.
+//  * fa_bwd_dkdv_kernel (D = 256): one workgroup of 4 wavefronts per (block
+//    of 128 keys, head, batch, head-dim half); each wave owns 32 keys and
+//    does both roles.  Its registers (about 440 per lane) allow one wavefront
+//    per SIMD, so each wave overlaps its own work: S and dP of the next query
+//    tile are computed while the weights and dS of the current one form.  The
+//    query tiles are 32 rows and the head dimensions of dK and dV are split
+//    between the two workgroups of a key block (both compute S and dP), so
+//    that a part's accumulators fit.
 //  * fa_bwd_dq_kernel: one workgroup of 8 wavefronts per (block of 256
 //    queries, head, batch), two wavefronts per SIMD as in the forward; waves
 //    0-3 issue the tile copies.  (D = 256: 4 wavefronts, 32-key tiles.)  The forward's layout (one query per lane):
