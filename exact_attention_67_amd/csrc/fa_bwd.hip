@@ -13,25 +13,18 @@
 //   dS    = P * (dP - Delta)
 //   dq    = scale * dS k,   dk = scale * dS^T q
 //
-// Three kernels (four templates):
+// Three kernels:
 //  * fa_bwd_delta_kernel: Delta (one row per TPR consecutive lanes).
-//  * fa_bwd_dkdv_pair_kernel (D = 64, 128): one workgroup of 8 wavefronts per
-//    (block of 128 keys, head, batch).  Waves w and w + 4 share a SIMD and own
-//    the same 32 keys; the P wave forms S = q K^T, the weights P and dV, and
-//    hands P to the dS wave through LDS, which forms dP = dO V^T, dS and dK
-//    one tile later.  S and dP come out with one key per lane (the forward's
+//  * fa_bwd_dkdv_pair_kernel: one workgroup of 8 wavefronts per (block of
+//    128 keys, head, batch).  Waves w and w + 4 share a SIMD and own the same
+//    32 keys; the P wave forms S = q K^T, the weights P and dV, and hands P
+//    to the dS wave through LDS, which forms dP = dO V^T, dS and dK one tile
+//    later.  S and dP come out with one key per lane (the forward's
 //    S^T = K Q^T with the roles of queries and keys exchanged), so P and dS
 //    are per-lane columns; dV += P^T dO and dK += dS^T q read dO and q with
 //    the transposing LDS read.  Each query tile of q and dO is copied once,
 //    in a swizzle that serves both the row reads and the transposing reads.
-//  * fa_bwd_dkdv_kernel (D = 256): one workgroup of 4 wavefronts per (block
-//    of 128 keys, head, batch, head-dim half); each wave owns 32 keys and
-//    does both roles.  Its registers (about 440 per lane) allow one wavefront
-//    per SIMD, so each wave overlaps its own work: S and dP of the next query
-//    tile are computed while the weights and dS of the current one form.  The
-//    query tiles are 32 rows and the head dimensions of dK and dV are split
-//    between the two workgroups of a key block (both compute S and dP), so
-//    that a part's accumulators fit.
+//    Query tiles are 64 rows (32 at D = 256).
 //  * fa_bwd_dq_kernel: one workgroup of 8 wavefronts per (block of 256
 //    queries, head, batch), two wavefronts per SIMD as in the forward; waves
 //    0-3 issue the tile copies.  (D = 256: 4 wavefronts, 32-key tiles.)  The forward's layout (one query per lane):
@@ -206,245 +199,8 @@ __device__ __forceinline__ void tr_chunk(f32x16 (&acc)[NB], const lds_u8* tile,
 }
 
 // ----------------------------------------------------------------------------
-// dK, dV: one workgroup per (128 keys, head, batch, head-dim part)
-// ----------------------------------------------------------------------------
-// Query tiles t stream through LDS.  Step t computes, on the matrix cores,
-// S(t+1) and dP(t+1) for the next tile while the weights P(t) and dS(t) form,
-// then dV += P(t)^T dO(t) and dK += dS(t)^T q(t).  Each q and dO tile is
-// stored once, in the swizzle that serves both its row reads (S, dP, one step
-// before its weights) and its transposed reads (dV, dK), in three stages:
-// during step t tile t+1 is read by rows, tile t transposed, and tile t+2
-// lands in the third.  LSE and Delta of tile t+1 land during step t.
-template <int D, int BQ, int NP, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void fa_bwd_dkdv_kernel(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-    const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-    const float* __restrict__ LSE, const float* __restrict__ Delta, uint16_t* __restrict__ dK,
-    uint16_t* __restrict__ dV, int S, int nk, int bh_total, int group_heads, float c,
-    float scale) {
-  using C = BfCfg<D, BQ, 4>;  // query tiles of BQ rows; 4 waves of 32 keys
-  // The head dimensions of dK and dV are split into NP parts, one workgroup
-  // each (NP = 2 at D = 256, where two full accumulators do not fit beside
-  // the K and V fragments); every part computes the full S and dP.
-  constexpr int NB = C::DB / NP;  // 32-wide head-dim blocks of this part
-  // Three stages of q and dO tiles, each a separately named array: the
-  // compiler then sees that a step's copies and its operand reads touch
-  // different arrays, and waits for the copies only where asked (the end of
-  // the step), not before the step's first read.
-  __shared__ __attribute__((aligned(1024))) uint8_t q0_raw[C::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t q1_raw[C::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t q2_raw[C::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t d0_raw[C::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t d1_raw[C::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t d2_raw[C::TILE_BYTES];
-  __shared__ __attribute__((aligned(256))) uint8_t ls0_raw[256];
-  __shared__ __attribute__((aligned(256))) uint8_t ls1_raw[256];
-  __shared__ __attribute__((aligned(256))) uint8_t de0_raw[256];
-  __shared__ __attribute__((aligned(256))) uint8_t de1_raw[256];
-  lds_u8* q0s = (lds_u8*)q0_raw;
-  lds_u8* q1s = (lds_u8*)q1_raw;
-  lds_u8* q2s = (lds_u8*)q2_raw;
-  lds_u8* d0s = (lds_u8*)d0_raw;
-  lds_u8* d1s = (lds_u8*)d1_raw;
-  lds_u8* d2s = (lds_u8*)d2_raw;
-  lds_u8* ls0 = (lds_u8*)ls0_raw;
-  lds_u8* ls1 = (lds_u8*)ls1_raw;
-  lds_u8* de0 = (lds_u8*)de0_raw;
-  lds_u8* de1 = (lds_u8*)de1_raw;
-
-  // Heaviest key blocks (the first ones, seen by most query tiles) first.
-  int bh, kt;
-  const int L = xcd_logical_index(blockIdx.x, nk * bh_total * NP);  // parts adjacent: same XCD
-  const int part = L % NP;
-  decode_tile<CAUSAL>(L / NP, nk, bh_total, group_heads, bh, kt);
-  if (CAUSAL) kt = nk - 1 - kt;
-
-  const size_t head = (size_t)bh * (size_t)S * D;
-  const uint16_t* Qh = Q + head;
-  const uint16_t* Kh = K + head;
-  const uint16_t* Vh = V + head;
-  const uint16_t* dOh = dO + head;
-  const float* LSEh = LSE + (size_t)bh * S;
-  const float* Dh = Delta + (size_t)bh * S;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int m = lane & 31;
-  const int hh = lane >> 5;
-  const int k0 = kt * 128;
-  const int kw0 = k0 + wave * kRowsPerWave;
-  const int my_k = kw0 + m;
-
-  // Query tiles this workgroup visits: causal -- those with a query >= k0.
-  // A wave takes part in tile t when some query of the tile sees one of its
-  // keys (with the causal mask this holds for every tile after its first).
-  const int nt = (S + BQ - 1) / BQ;
-  const int t_first = CAUSAL ? k0 / BQ : 0;
-  auto live = [&](int t) { return kw0 < S && (!CAUSAL || t * BQ + BQ - 1 >= kw0); };
-
-  int off[C::LOADS_PER_WAVE], row[C::LOADS_PER_WAVE];
-  tile_offsets_u<C>(off, row, wave, lane);
-  auto copy_tile = [&](int t, lds_u8* qd, lds_u8* dd) {
-    const int q0 = t * BQ;
-    issue_tile<C>(Qh, qd, q0, S, wave, off, row);
-    issue_tile<C>(dOh, dd, q0, S, wave, off, row);
-  };
-  auto copy_vecs = [&](int t, lds_u8* ls, lds_u8* de) {
-    const int q0 = t * BQ;
-    if (wave == 0) issue_rowvec(LSEh, ls, q0, S, lane);
-    if (wave == 1) issue_rowvec(Dh, de, q0, S, lane);
-  };
-
-  bf16x8 kf[C::KCH], vf[C::KCH];
-  // negative scale: S from -K with |c| (see kZeroScaleC); dK uses q as it is
-  row_fragments<C>(kf, Kh, my_k, S, hh, sign_flip_mask(c));
-  row_fragments<C>(vf, Vh, my_k, S, hh);
-  c = fabsf(c);
-  int k_off[C::NKOFF], v_off[C::NVOFF], v_hi[C::NVOFF];
-  operand_offsets_u<C>(lane, k_off, v_off, v_hi);
-
-  f32x16 dk_acc[NB], dv_acc[NB];
-#pragma unroll
-  for (int db = 0; db < NB; ++db) {
-    dk_acc[db] = f32x16{};
-    dv_acc[db] = f32x16{};
-  }
-
-  if (t_first < nt) {
-    copy_tile(t_first, q0s, d0s);
-    copy_vecs(t_first, ls0, de0);
-  }
-  if (t_first + 1 < nt) copy_tile(t_first + 1, q1s, d1s);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  // S and dP tiles in two named sets used alternately.
-  f32x16 s_a[C::KB], dp_a[C::KB], s_b[C::KB], dp_b[C::KB];
-  if (t_first < nt && live(t_first)) {
-#pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb) {
-      qk_block<C>(s_a[kb], q0s, kf, k_off, kb);
-      qk_block<C>(dp_a[kb], d0s, vf, k_off, kb);
-    }
-  }
-  // (step t_first copies into the third slot and the second LSE/Delta
-  // buffers, which nothing has read yet: no barrier needed here)
-
-  // Step t: q and dO of tile t in qt, dt (read transposed), of tile t+1 in
-  // qr_n, dr_n (read by rows); tile t+2 lands in q_l, d_l, and LSE, Delta of
-  // tile t+1 in ls_l, de_l.  S(t+1), dP(t+1) go to s_out, dp_out while P(t),
-  // dS(t) form from s_in, dp_in; then the dV and dK products of tile t.
-  auto step = [&](const int t, const lds_u8* qt, const lds_u8* dt, const lds_u8* qr_n,
-                  const lds_u8* dr_n, lds_u8* q_l, lds_u8* d_l, const lds_u8* ls,
-                  const lds_u8* de, lds_u8* ls_l, lds_u8* de_l, f32x16 (&s_in)[C::KB],
-                  f32x16 (&dp_in)[C::KB], f32x16 (&s_out)[C::KB], f32x16 (&dp_out)[C::KB]) {
-    if (t + 2 < nt) copy_tile(t + 2, q_l, d_l);
-    if (t + 1 < nt) copy_vecs(t + 1, ls_l, de_l);
-    const int q0 = t * BQ;
-    if (live(t)) {
-      // ---- mask (diagonal and tail tiles): excluded scores -> -inf ------------
-      if ((CAUSAL && q0 < kw0 + 31) || (q0 + BQ > S)) {
-#pragma unroll
-        for (int qb = 0; qb < C::KB; ++qb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            // register r of block qb holds query row 32*qb + 16*(r/8) + 8*hh + r%8
-            const int q = q0 + 32 * qb + 16 * (r >> 3) + 8 * hh + (r & 7);
-            if (q >= S || (CAUSAL && my_k > q)) s_in[qb][r] = -INFINITY;
-          }
-      }
-      bf16x8 pq[C::PCH], dsq[C::PCH];
-      // weights and dS of the 16-query chunk pc (registers 8*half .. +7 of block qb)
-      auto chunk = [&](int qb, int half) {
-        const int rb = 32 * qb + 16 * half + 8 * hh;
-        const int pc = 2 * qb + half;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int r = 8 * half + e;
-          const float lse2 = reinterpret_cast<const lds_f32*>(ls)[rb + e] * kLog2e;
-          const float del = reinterpret_cast<const lds_f32*>(de)[rb + e];
-          const float p = fast_exp2(fmaf(s_in[qb][r], c, -lse2));
-          pq[pc][e] = (__bf16)p;
-          dsq[pc][e] = (__bf16)(p * (dp_in[qb][r] - del));
-        }
-      };
-      // The products of a 16-query chunk follow the chunk's weights, and
-      // S(t+1), dP(t+1) are split around them, so the matrix cores always
-      // have independent work while the weights form.  The compiler's
-      // MFMA/LDS interleave strategy 1 orders the region (measured: 3-6 %
-      // faster than its default order; pinning the order with scheduling
-      // group barriers, as the forward does, was 7 % slower).
-#pragma unroll
-      for (int qb = 0; qb < C::KB; ++qb) {
-        qk_block<C>(s_out[qb], qr_n, kf, k_off, qb);
-        qk_block<C>(dp_out[qb], dr_n, vf, k_off, qb);
-        chunk(qb, 0);
-        chunk(qb, 1);
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int pc = 2 * qb + half;
-          tr_chunk<C, NB>(dv_acc, dt, pq[pc], v_off, v_hi, pc, part);   // dV^T += dO^T P
-          tr_chunk<C, NB>(dk_acc, qt, dsq[pc], v_off, v_hi, pc, part);  // dK^T += q^T dS
-        }
-      }
-      __builtin_amdgcn_iglp_opt(1);
-    } else if (t + 1 < nt && live(t + 1)) {
-      // the wave's first tile is the next one: only S(t+1), dP(t+1)
-#pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb) {
-        qk_block<C>(s_out[kb], qr_n, kf, k_off, kb);
-        qk_block<C>(dp_out[kb], dr_n, vf, k_off, kb);
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-  };
-  // Six steps per pass: the three stages rotate, and the S/dP sets and the
-  // LSE/Delta buffers alternate, with every buffer named at compile time.
-  if (t_first < nt) {
-    for (int t = t_first;;) {
-      step(t, q0s, d0s, q1s, d1s, q2s, d2s, ls0, de0, ls1, de1, s_a, dp_a, s_b, dp_b);
-      if (++t >= nt) break;
-      step(t, q1s, d1s, q2s, d2s, q0s, d0s, ls1, de1, ls0, de0, s_b, dp_b, s_a, dp_a);
-      if (++t >= nt) break;
-      step(t, q2s, d2s, q0s, d0s, q1s, d1s, ls0, de0, ls1, de1, s_a, dp_a, s_b, dp_b);
-      if (++t >= nt) break;
-      step(t, q0s, d0s, q1s, d1s, q2s, d2s, ls1, de1, ls0, de0, s_b, dp_b, s_a, dp_a);
-      if (++t >= nt) break;
-      step(t, q1s, d1s, q2s, d2s, q0s, d0s, ls0, de0, ls1, de1, s_a, dp_a, s_b, dp_b);
-      if (++t >= nt) break;
-      step(t, q2s, d2s, q0s, d0s, q1s, d1s, ls1, de1, ls0, de0, s_b, dp_b, s_a, dp_a);
-      if (++t >= nt) break;
-    }
-  }
-
-  if (my_k >= S) return;
-  store_col<NB>(dK + head + (size_t)my_k * D + part * NB * 32, dk_acc, scale, hh);
-  store_col<NB>(dV + head + (size_t)my_k * D + part * NB * 32, dv_acc, 1.0f, hh);
-}
-
-// acc[db] += A^T * bf, A read transposed from a tile in the unified swizzle.
-template <class C>
-__device__ __forceinline__ void tr_product_u(f32x16 (&acc)[C::DB], const lds_u8* tile,
-                                             const bf16x8 (&bf)[C::PCH],
-                                             const int (&v_off)[C::NVOFF],
-                                             const int (&v_hi)[C::NVOFF]) {
-#pragma unroll
-  for (int pc = 0; pc < C::PCH; ++pc)
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db) {
-      const lds_u8* b = tile + pc * 16 * C::ROW_BYTES + (db / C::NVOFF) * 256;
-      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b + v_off[db % C::NVOFF]));
-      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b + v_hi[db % C::NVOFF]));
-      const bf16x8 af =
-          __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf[pc], acc[db], 0, 0, 0);
-    }
-}
-
-// ----------------------------------------------------------------------------
-// dK, dV with wave pairs (D = 64, 128): one workgroup of 8 wavefronts per
-// (block of 128 keys, head, batch)
+// dK, dV with wave pairs: one workgroup of 8 wavefronts per (block of 128
+// keys, head, batch)
 // ----------------------------------------------------------------------------
 // Waves w and w + 4 run on the same SIMD and own the same 32 keys; they split
 // the work on each 64-query tile.  The P wave computes S = q K^T, the weights
@@ -467,10 +223,12 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_pair_kernel(
     const float* __restrict__ LSE, const float* __restrict__ Delta, uint16_t* __restrict__ dK,
     uint16_t* __restrict__ dV, int S, int nk, int bh_total, int group_heads, float c,
     float scale) {
-  constexpr int BQ = 64;
+  // Query tiles of 64 rows, 32 at D = 256 (registers: the key fragment and
+  // the accumulator alone take 192 of a wave's 256 there).
+  constexpr int BQ = D == 256 ? 32 : 64;
   using C = BfCfg<D, BQ, 4>;        // tile geometry; each role copies its tensor in 4 parts
   constexpr int XB = C::PCH * 1024;  // P of one pair and tile: PCH chunks x 64 lanes x 16 B
-  static_assert(C::KB == 2 && C::PCH == 4, "64-query tiles");
+  static_assert(C::PCH == 2 * C::KB, "two 16-query chunks per 32-query block");
   __shared__ __attribute__((aligned(1024))) uint8_t q0_raw[C::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t q1_raw[C::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t q2_raw[C::TILE_BYTES];
@@ -621,8 +379,14 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_pair_kernel(
   };
   auto d_step = [&](const int t, const lds_u8* dsr, const lds_u8* qprev, const lds_u8* eprev,
                     const lds_u8* xs, f32x16 (&dp_out)[C::KB], const f32x16 (&dp_in)[C::KB]) {
-    if (t < nt) d_dp(t, dsr, dp_out);
-    if (t > t_first) d_ds(t - 1, qprev, eprev, xs, dp_in);
+    if constexpr (D == 256) {
+      // one dP set: dS(t-1) consumes it before dP(t) overwrites it
+      if (t > t_first) d_ds(t - 1, qprev, eprev, xs, dp_in);
+      if (t < nt) d_dp(t, dsr, dp_out);
+    } else {
+      if (t < nt) d_dp(t, dsr, dp_out);
+      if (t > t_first) d_ds(t - 1, qprev, eprev, xs, dp_in);
+    }
   };
 
   if (t_first < nt) copy_tile(t_first, q0s, d0s, l0s, e0s);
@@ -666,7 +430,12 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_pair_kernel(
   if (t < nt) {                 \
     FA_PAIR_END                 \
   }
-  f32x16 dp_a[C::KB], dp_b[C::KB];  // dP of the current and the previous tile
+  // dP of the current and the previous tile (at D = 256 one set serves both)
+  f32x16 dp_a[C::KB], dp_x[C::KB];
+  f32x16(&dp_b)[C::KB] = [&]() -> f32x16(&)[C::KB] {
+    if constexpr (D == 256) return dp_a;
+    else return dp_x;
+  }();
   if (t_first < nt) {
     for (int t = t_first;;) {
       FA_PAIR_COPY(q1s, d1s, l1s, e1s) d_step(t, d0s, q2s, e2s, x1s, dp_a, dp_b); FA_PAIR_DEND
@@ -687,6 +456,25 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_pair_kernel(
 #undef FA_PAIR_COPY
 #undef FA_PAIR_END
   if (my_k < S) store_col<C::DB>(dK + head + (size_t)my_k * D, acc, scale, hh);
+}
+
+// acc[db] += A^T * bf, A read transposed from a tile in the unified swizzle.
+template <class C>
+__device__ __forceinline__ void tr_product_u(f32x16 (&acc)[C::DB], const lds_u8* tile,
+                                             const bf16x8 (&bf)[C::PCH],
+                                             const int (&v_off)[C::NVOFF],
+                                             const int (&v_hi)[C::NVOFF]) {
+#pragma unroll
+  for (int pc = 0; pc < C::PCH; ++pc)
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      const lds_u8* b = tile + pc * 16 * C::ROW_BYTES + (db / C::NVOFF) * 256;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b + v_off[db % C::NVOFF]));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b + v_hi[db % C::NVOFF]));
+      const bf16x8 af =
+          __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf[pc], acc[db], 0, 0, 0);
+    }
 }
 
 // ----------------------------------------------------------------------------
@@ -829,27 +617,17 @@ int run_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint1
   int st = launch_k(fa_bwd_delta_kernel<D>, (unsigned)((rows * (D / 8) + 255) / 256), 256, s,
                     o, dout, delta, rows);
   if (st != FA_OK) return st;
-  // D = 256: 32-row query tiles (dK/dV) and 32-key tiles in 4-wave dQ
-  // workgroups (LDS and registers); otherwise 64 and 8 waves.
+  // dQ: 8 waves and 64-key tiles; D = 256: 4 waves and 32-key tiles
+  // (registers and LDS).
   constexpr int BT = D == 256 ? 32 : 64;
   constexpr int QW = D == 256 ? 4 : 8;
-  constexpr int NP = D == 256 ? 2 : 1;  // head-dim parts of dK/dV
   const int nk = (S + 127) / 128;
-  const unsigned grid = (unsigned)nk * (unsigned)bh * NP;
-  if constexpr (D != 256) {
-    if (causal)
-      st = launch_k(fa_bwd_dkdv_pair_kernel<D, true>, grid, 512, s, q, k, v, dout,
-                    (const float*)lse, (const float*)delta, dk, dv, S, nk, bh, group_heads, c,
-                    scale);
-    else
-      st = launch_k(fa_bwd_dkdv_pair_kernel<D, false>, grid, 512, s, q, k, v, dout,
-                    (const float*)lse, (const float*)delta, dk, dv, S, nk, bh, group_heads, c,
-                    scale);
-  } else if (causal)
-    st = launch_k(fa_bwd_dkdv_kernel<D, BT, NP, true>, grid, 256, s, q, k, v, dout,
+  const unsigned grid = (unsigned)nk * (unsigned)bh;
+  if (causal)
+    st = launch_k(fa_bwd_dkdv_pair_kernel<D, true>, grid, 512, s, q, k, v, dout,
                   (const float*)lse, (const float*)delta, dk, dv, S, nk, bh, group_heads, c, scale);
   else
-    st = launch_k(fa_bwd_dkdv_kernel<D, BT, NP, false>, grid, 256, s, q, k, v, dout,
+    st = launch_k(fa_bwd_dkdv_pair_kernel<D, false>, grid, 512, s, q, k, v, dout,
                   (const float*)lse, (const float*)delta, dk, dv, S, nk, bh, group_heads, c, scale);
   if (st != FA_OK) return st;
   const int nq = (S + 32 * QW - 1) / (32 * QW);
