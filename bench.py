@@ -176,7 +176,7 @@ def kernel_name(w, causal) -> str:
     plan = fa.fa_fwd_plan(w.B, w.H, w.S, w.D, int(causal), 2)
     waves, bc = plan["threads"] // 64, plan["keys_per_tile"]
     if w.D == 256:
-        return f"fa_fwd_bf16_ring_kernel<{w.D},{bc},{waves},{c}>"
+        return f"fa_fwd_bf16_pair_kernel<{c}>"
     return f"fa_fwd_bf16_kernel<{w.D},{bc},{waves},{c},true>"
 
 
@@ -286,9 +286,10 @@ def time_secondary(steps):
 # questions): the bf16 forward with its K/V tiles copied one step ahead (the
 # library), copied and waited for in the step that reads them, or copied two
 # or three steps ahead into three or four buffers each, and the products with
-# their operand reads alone (no copies, no exponentials).
+# their operand reads alone (no copies, no exponentials); at D = 256 the
+# library's wave-pair kernel against the one-wave ring kernel (ring256).
 STUDY_WORKLOADS = (("c4_bf16_causal_1x32x16384x128", True), ("c3_bf16_2x16x4096x128", True),
-                   ("c3_bf16_2x16x4096x128", False))
+                   ("c3_bf16_2x16x4096x128", False), ("c5_bf16_causal_2x8x8192x256_stress", True))
 
 
 def pipeline_study(rounds=3):

@@ -35,7 +35,8 @@ ABI_VERSION = 1
 # Pipeline-study builds of the same library: the bf16 forward's K/V tile
 # pipeline in another mode (FA_PIPE at build time; see the pipeline modes in
 # csrc/fa_fwd.hip).  Everything else is the same code.
-PIPE_VARIANTS = {"noprefetch": 1, "ksplit": 2, "ring3": 3, "ring4": 4, "mfma_only": 5}
+PIPE_VARIANTS = {"noprefetch": 1, "ksplit": 2, "ring3": 3, "ring4": 4, "mfma_only": 5,
+                 "ring256": 6}
 
 _lock = threading.Lock()
 _lib = None

@@ -97,6 +97,9 @@ constexpr float kRescaleThreshold = 24.0f;
 // Largest sum of one lane's softmax weights in a tile (32 keys) that the
 // kernels accept without moving the row's reference max.
 constexpr float kRowSumLimit = 4096.0f;
+// The same limit for the D = 256 kernel: 2^kRescaleThreshold, so that no
+// weight exceeds 2^24 (a sum within it bounds each of its terms).
+constexpr float kPairSumLimit = 16777216.0f;
 
 template <int D_, int BC_, int WAVES_>
 struct BfCfg {

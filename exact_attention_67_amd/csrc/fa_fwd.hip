@@ -86,6 +86,8 @@ enum PipeMode : int {
   kPipeRing4 = 4,       // four buffers each; a tile is copied three steps before it is read
   kPipeMfmaOnly = 5,    // no copies, no exponentials, no weight check: the products and
                         // their LDS operand reads alone (a timing probe; results are void)
+  kPipeD256Ring = 6,    // D = 256 on fa_fwd_bf16_ring_kernel (one wave per SIMD) in place
+                        // of the wave-pair kernel; D <= 128 as kPipeOverlap
 };
 template <int PIPE>
 struct PipeCfg {
@@ -100,7 +102,8 @@ struct PipeCfg {
 #endif
 constexpr int kPipe = FA_PIPE;
 static_assert(kPipe == kPipeOverlap || kPipe == kPipeNoPrefetch || kPipe == kPipeKSplit ||
-                  kPipe == kPipeRing3 || kPipe == kPipeRing4 || kPipe == kPipeMfmaOnly,
+                  kPipe == kPipeRing3 || kPipe == kPipeRing4 || kPipe == kPipeMfmaOnly ||
+                  kPipe == kPipeD256Ring,
               "FA_PIPE");
 
 // sched_group_barrier with a compile-time count; nothing when the count is 0.
@@ -1149,6 +1152,405 @@ __global__ __launch_bounds__(64 * WAVES, D <= 128 ? 2 : 1) void fa_fwd_bf16_ring
 }
 
 // ----------------------------------------------------------------------------
+// bf16 kernel on wave pairs (D = 256)
+// ----------------------------------------------------------------------------
+// Eight waves, two per SIMD, in four pairs; pair p owns query rows
+// [32p, 32p + 32) of the workgroup's 128.  The S wave of a pair (waves 0-3)
+// forms the scores, the row maxima and the softmax weights; the O wave (waves
+// 4-7, on the same SIMD as its S wave) accumulates O from the weights and V,
+// and issues every K/V tile copy.  Each does 16 of the 32 matrix-core
+// products of a 32-key tile, so neither repeats work, and the S wave's
+// exponentials overlap the O wave's products on the SIMD.  The weights P(t)
+// of tile t (bf16, the B operand of the P.V product exactly as the S wave
+// holds it) pass through LDS with the reference max they were taken against;
+// the O wave rescales O when that reference moved.
+//
+// Step j (one workgroup barrier each): the S wave forms S(j+3) from K(j+3)
+// and the weights P(j+2) of S(j+2); the O wave adds V(j) P(j), with P(j) in
+// registers since step j-1, and reads P(j+1) for the next step, so that no
+// LDS wait sits between the barrier and its first product.  It also issues
+// the copies of K(j+5) and V(j+3), each waited for at the end of step j+1.
+// K and V each have four LDS buffers.  Softmax: as in the ring kernel
+// (reference max from tile 0, raised only past kRescaleThreshold).
+template <bool CAUSAL>
+__global__ __launch_bounds__(512, 1) void fa_fwd_bf16_pair_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
+    int Sq, int Sk, int nq, int bh_total, int group_heads, float c) {
+  using C = BfCfg<256, 32, 4>;  // tile geometry: 128 query rows, 32-key tiles
+  constexpr int D = C::D, BC = C::BC;
+  constexpr int NL = C::LOADS_PER_WAVE;  // copy pieces per tensor per O wave
+  static_assert(C::BR == 4 * kRowsPerWave && C::COPY_WAVES == 4 && C::KB == 1 && C::PCH == 2,
+                "pair kernel: four pairs of 32 rows, one 32-key block per tile");
+  // negative scale: S from -Q with |c| (see kZeroScaleC)
+  const uint32_t qflip = sign_flip_mask(c);
+  c = fabsf(c);
+  __shared__ __attribute__((aligned(1024))) uint8_t kb0_raw[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t kb1_raw[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t kb2_raw[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t kb3_raw[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vb0_raw[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vb1_raw[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vb2_raw[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vb3_raw[C::TILE_BYTES];
+  // P(t) of the four pairs for t even / odd: 2 KiB per pair, chunk pc of lane
+  // l at pc * 1024 + 16 l (no bank conflict on either side).
+  __shared__ __attribute__((aligned(1024))) uint8_t xp0_raw[4 * 2048];
+  __shared__ __attribute__((aligned(1024))) uint8_t xp1_raw[4 * 2048];
+  // the reference max of P(t) per row (t even / odd)
+  __shared__ float xm0[C::BR], xm1[C::BR];
+  lds_u8* kb0 = (lds_u8*)kb0_raw;
+  lds_u8* kb1 = (lds_u8*)kb1_raw;
+  lds_u8* kb2 = (lds_u8*)kb2_raw;
+  lds_u8* kb3 = (lds_u8*)kb3_raw;
+  lds_u8* vb0 = (lds_u8*)vb0_raw;
+  lds_u8* vb1 = (lds_u8*)vb1_raw;
+  lds_u8* vb2 = (lds_u8*)vb2_raw;
+  lds_u8* vb3 = (lds_u8*)vb3_raw;
+  lds_u8* xp0 = (lds_u8*)xp0_raw;
+  lds_u8* xp1 = (lds_u8*)xp1_raw;
+
+  int bh, qt;
+  decode_tile<CAUSAL>(xcd_logical_index(blockIdx.x, nq * bh_total), nq, bh_total,
+                      group_heads, bh, qt);
+  const size_t qhead = (size_t)bh * (size_t)Sq * D;
+  const size_t khead = (size_t)bh * (size_t)Sk * D;
+  const uint16_t* Qh = Q + qhead;
+  const uint16_t* Kh = K + khead;
+  const uint16_t* Vh = V + khead;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pair = wave & 3;
+  const int m = lane & 31;
+  const int hh = lane >> 5;
+  const int q0 = qt * C::BR;
+  const int qw0 = q0 + pair * kRowsPerWave;
+  const int my_q = qw0 + m;
+  // bottom-right causal alignment, as in the other kernels
+  const int kshift = Sk - Sq;
+  const int kend = CAUSAL ? max(0, min(Sk, q0 + C::BR + kshift)) : Sk;
+  const int ntiles = (kend + BC - 1) / BC;
+  const int pair_klast = CAUSAL ? min(qw0 + kRowsPerWave - 1 + kshift, Sk - 1) : (Sk - 1);
+  const int wnt = (qw0 < Sq && pair_klast >= 0) ? min(ntiles, pair_klast / BC + 1) : 0;
+  const int xoff = pair * 2048 + lane * 16;  // this lane's P chunk 0
+  const int moff = pair * kRowsPerWave + m;  // this lane's row in xm
+
+  // The O wave of pair p issues share p of every K and V tile copy.
+  int koff[NL], krow[NL], voff[NL], vrow[NL];
+  tile_offsets<C, false>(koff, krow, pair, lane);
+  tile_offsets<C, true>(voff, vrow, pair, lane);
+  const int wslot = pair * (NL * 1024);  // this wave's share of a buffer
+  // Copy of tile t (the last tile past the end, so that every step issues
+  // the same number of copies).
+  const auto copy = [&](const uint16_t* src, int t, const int* off, const int* row,
+                        lds_u8* dst) {
+    const char* b;
+    int bo[NL];
+    tile_src<C>(src, min(t, ntiles - 1) * BC, Sk, off, row, b, bo);
+#pragma unroll
+    for (int u = 0; u < NL; ++u) copy_piece(b, bo[u], dst + wslot + u * 1024);
+  };
+  const auto prologue_copies = [&]() {
+    if (ntiles > 0) {
+      copy(Kh, 0, koff, krow, kb0);
+      copy(Kh, 1, koff, krow, kb1);
+      copy(Kh, 2, koff, krow, kb2);
+      copy(Kh, 3, koff, krow, kb3);
+      copy(Vh, 0, voff, vrow, vb0);
+      copy(Vh, 1, voff, vrow, vb1);
+    }
+  };
+
+  if (wave < 4) {
+    // ---------------- S wave: scores, weights, row sums, LSE ----------------
+    bf16x8 qf[C::KCH];
+#pragma unroll
+    for (int ch = 0; ch < C::KCH; ++ch) {
+      u32x4 raw = u32x4{0u, 0u, 0u, 0u};
+      if (my_q < Sq)
+        raw = *reinterpret_cast<const u32x4*>(Qh + (size_t)my_q * D + ch * 16 + hh * 8);
+      qf[ch] = __builtin_bit_cast(bf16x8, raw ^ qflip);
+    }
+    const int pm = key_perm(m);
+    const int ksw = kswz<C>(pm);
+    int k_off[C::NKOFF];
+#pragma unroll
+    for (int b = 0; b < C::NKOFF; ++b)
+      k_off[b] = pm * C::ROW_BYTES + (((2 * b + hh) ^ ksw) << 4);
+
+    float m_run = -INFINITY;
+    float l_exact = 0.0f;  // float32 sum of the weights (for the LSE)
+    f32x16 s_a[1], s_b[1];
+
+    const auto needs_mask = [&](int t) {
+      const int k0 = t * BC;
+      return (CAUSAL && (k0 + BC - 1 > qw0 + kshift)) || (k0 + BC > Sk);
+    };
+    const auto mask_tile = [&](f32x16 (&s)[1], int k0) {
+      const int lim = (CAUSAL ? min(my_q + kshift, Sk - 1) : (Sk - 1)) - k0 - hh * 8;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = (r >> 3) * 16 + (r & 7);
+        s[0][r] = key > lim ? -INFINITY : s[0][r];
+      }
+    };
+    // Weights of the tile in s against m_run (bf16, in the layout of the B
+    // operand of the P.V product) and their float32 sum.
+    const auto weights = [&](const f32x16 (&s)[1], bf16x8 (&pf)[2], float& rs) {
+      const float mc = m_run == -INFINITY ? 0.0f : m_run * c;
+      rs = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(fmaf(s[0][r], c, -mc));
+        rs += p;
+        pf[r >> 3][r & 7] = (__bf16)p;
+      }
+    };
+    // The rare path: a lane's weights sum past kPairSumLimit (or not to a
+    // finite value).  Raise the reference to the row max seen so far and form
+    // the tile's weights again (the O wave rescales O when it sees the new
+    // reference next to them).
+    const auto raise = [&](const f32x16 (&s)[1], bf16x8 (&pf)[2], float& rs) {
+      // (the weights formed before are replaced; this use keeps their
+      // computation where the instruction order put it, and the pass of the
+      // scores through it keeps this path's work out of the common one)
+      f32x16 sr[1] = {s[0]};
+      asm volatile("" : "+v"(sr[0]) : "v"(pf[0]), "v"(pf[1]));
+      const float mt = row_max<C>(sr, hh);
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = m_new == m_run ? 1.0f : fast_exp2((m_run - m_new) * c);
+      m_run = m_new;
+      l_exact *= alpha;
+      weights(sr, pf, rs);
+    };
+    // Weights of tile t for the O wave: P and its reference to LDS.
+    const auto publish = [&](const f32x16 (&s)[1], lds_u8* xp, float* xm) {
+      bf16x8 pf[2];
+      float rs;
+      weights(s, pf, rs);
+      if (__any(!(rs <= kPairSumLimit))) raise(s, pf, rs);
+      *(lds_bf16x8*)(xp + xoff) = pf[0];
+      *(lds_bf16x8*)(xp + xoff + 1024) = pf[1];
+      xm[moff] = m_run;
+      l_exact += rs;
+    };
+
+    __syncthreads();  // K(0..3), V(0..1) are in LDS
+    // P(0), P(1) and S(2).  The reference max comes from S(0) (masked): every
+    // row that sees any key sees key 0, so only rows that see nothing keep
+    // -inf.
+    if (wnt > 0) {
+      qk_tile<C>(s_b, kb0, qf, k_off);
+      if (needs_mask(0)) mask_tile(s_b, 0);
+      m_run = row_max<C>(s_b, hh);
+      publish(s_b, xp0, xm0);
+      if (wnt > 1) {
+        qk_tile<C>(s_b, kb1, qf, k_off);
+        if (needs_mask(1)) mask_tile(s_b, BC);
+        publish(s_b, xp1, xm1);
+      }
+      if (wnt > 2) qk_tile<C>(s_a, kb2, qf, k_off);
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));
+    plain_barrier();
+    plain_barrier();  // the O waves have read P(0): its buffer takes P(2)
+
+    // step j: S(j+3) into s_out, the weights of S(j+2) (in s_in) to xp
+    const auto s_step = [&](const int j, const lds_u8* k_rd, f32x16 (&s_in)[1],
+                            f32x16 (&s_out)[1], lds_u8* xp, float* xm) {
+      const int t = j + 2;  // the tile whose weights this step forms
+      if (t + 1 < wnt && !needs_mask(t)) {
+        qk_tile<C>(s_out, k_rd, qf, k_off);
+        publish(s_in, xp, xm);
+        // each product followed by one K read (kLead ahead) and 4 VALU
+        constexpr int kLead = 3;
+        __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);
+#pragma unroll
+        for (int i = 0; i < C::KCH; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        }
+      } else if (t < wnt) {  // a masked tile, or the pair's last
+        if (needs_mask(t)) mask_tile(s_in, t * BC);
+        if (t + 1 < wnt) qk_tile<C>(s_out, k_rd, qf, k_off);
+        publish(s_in, xp, xm);
+      }
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));
+      plain_barrier();
+    };
+    // S(t) lives in s_a for t even, s_b for t odd; K(t) in kb(t mod 4); P(t)
+    // in xp(t mod 2).
+#define FA_S_STEP(J, POS)                                              \
+  ((POS) == 0   ? s_step(J, kb3, s_a, s_b, xp0, xm0)                   \
+   : (POS) == 1 ? s_step(J, kb0, s_b, s_a, xp1, xm1)                   \
+   : (POS) == 2 ? s_step(J, kb1, s_a, s_b, xp0, xm0)                   \
+                : s_step(J, kb2, s_b, s_a, xp1, xm1))
+    int j = 0;
+    for (; j + 4 <= ntiles; j += 4) {
+      FA_S_STEP(j, 0);
+      FA_S_STEP(j + 1, 1);
+      FA_S_STEP(j + 2, 2);
+      FA_S_STEP(j + 3, 3);
+    }
+    if (j < ntiles) FA_S_STEP(j, 0);
+    if (j + 1 < ntiles) FA_S_STEP(j + 1, 1);
+    if (j + 2 < ntiles) FA_S_STEP(j + 2, 2);
+#undef FA_S_STEP
+
+    const float le = l_exact + swap_halves(l_exact, hh);
+    // A row that saw no key keeps m_run = -inf and le = 0: LSE = -inf.
+    if (my_q < Sq && hh == 0) LSE[(size_t)bh * Sq + my_q] = (m_run * c + fast_log2(le)) * kLn2;
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));
+    plain_barrier();
+    return;
+  }
+
+  // ---------------- O wave: O += V P, the tile copies ----------------
+  // The O wave's instructions win the SIMD's issue arbitration over its S
+  // wave's: its step is the longer one (the S wave waits at the barrier).
+  __builtin_amdgcn_s_setprio(1);
+  prologue_copies();
+  const int g = lane >> 4, j4 = (lane >> 2) & 3, t4 = lane & 3;
+  const int vx = 2 * (g & 1) + (t4 >> 1);
+  const int vsw = vswz<C>(hh * 8 + j4);
+  const int v_row = (hh * 8 + j4) * C::ROW_BYTES + (t4 & 1) * 8;
+  int v_off[C::NVOFF];
+#pragma unroll
+  for (int d4 = 0; d4 < C::NVOFF; ++d4) v_off[d4] = v_row + (((4 * d4 + vx) ^ vsw) << 4);
+  f32x16 acc[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
+
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();  // K(0..3), V(0..1) are in LDS
+  if (ntiles > 0) copy(Vh, 2, voff, vrow, vb2);
+  plain_barrier();  // P(0), P(1) and their references are in LDS
+  if (ntiles > 0) copy(Kh, 4, koff, krow, kb0);
+  // the weights for this step and the reference they were taken against
+  bf16x8 pf[2];
+  float m_p = -INFINITY;
+  if (wnt > 0) {
+    pf[0] = *(const lds_bf16x8*)(xp0 + xoff);
+    pf[1] = *(const lds_bf16x8*)(xp0 + xoff + 1024);
+    m_p = xm0[moff];
+  }
+  float m_b = m_p;  // the reference O is scaled to
+  // sum of the bf16 weights (two chains), the normalisation of O
+  float l_round0 = 0.0f, l_round1 = 0.0f;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));
+  plain_barrier();  // P(0) is read: step 0 of the S waves overwrites it
+
+  const auto o_step = [&](const int j, const lds_u8* v_rd, lds_u8* k_wr, lds_u8* v_wr,
+                          const lds_u8* xp_next, const float* xm_next) {
+    if (j < wnt) {
+      if (__any(m_p != m_b)) {
+        const float alpha = m_p == m_b ? 1.0f : fast_exp2((m_b - m_p) * c);
+        m_b = m_p;
+        l_round0 *= alpha;
+        l_round1 *= alpha;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) acc[db] *= alpha;
+      }
+#pragma unroll
+      for (int pc = 0; pc < 2; ++pc)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const bf16x2 two = {pf[pc][2 * t], pf[pc][2 * t + 1]};
+          if (pc & 1) l_round1 = __builtin_amdgcn_fdot2_f32_bf16(two, ones, l_round1, false);
+          else l_round0 = __builtin_amdgcn_fdot2_f32_bf16(two, ones, l_round0, false);
+        }
+      // P(j+1) for the next step (written during step j-1)
+      bf16x8 pn[2];
+      float mn = m_p;
+      if (j + 1 < wnt) {
+        pn[0] = *(const lds_bf16x8*)(xp_next + xoff);
+        pn[1] = *(const lds_bf16x8*)(xp_next + xoff + 1024);
+        mn = xm_next[moff];
+      }
+      copy(Kh, j + 5, koff, krow, k_wr);
+      copy(Vh, j + 3, voff, vrow, v_wr);
+#pragma unroll
+      for (int pc = 0; pc < C::PCH; ++pc)
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          const lds_u8* p = v_rd + pc * 16 * C::ROW_BYTES + (db / C::NVOFF) * 256 +
+                            v_off[db % C::NVOFF];
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+          const s16x4 hi =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * C::ROW_BYTES));
+          const bf16x8 vf = __builtin_bit_cast(
+              bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[pc], acc[db], 0, 0, 0);
+        }
+      // each product's two V reads issued kLead products ahead, one copy
+      // after every second product
+      constexpr int kLead = 3;
+      constexpr int kNM = C::DB * C::PCH;
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kLead, 0);
+#pragma unroll
+      for (int i = 0; i < kNM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i + kLead < kNM) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        if (i & 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+      if (j + 1 < wnt) {
+        pf[0] = pn[0];
+        pf[1] = pn[1];
+        m_p = mn;
+      }
+    } else {
+      copy(Kh, j + 5, koff, krow, k_wr);
+      copy(Vh, j + 3, voff, vrow, v_wr);
+    }
+    // The previous step's copies have landed (this step's stay in flight).
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * NL));
+    plain_barrier();
+  };
+  // V(t) in vb(t mod 4), K(t) in kb(t mod 4), P(t) in xp(t mod 2)
+#define FA_O_STEP(J, POS)                                          \
+  ((POS) == 0   ? o_step(J, vb0, kb1, vb3, xp1, xm1)               \
+   : (POS) == 1 ? o_step(J, vb1, kb2, vb0, xp0, xm0)               \
+   : (POS) == 2 ? o_step(J, vb2, kb3, vb1, xp1, xm1)               \
+                : o_step(J, vb3, kb0, vb2, xp0, xm0))
+  int j = 0;
+  for (; j + 4 <= ntiles; j += 4) {
+    FA_O_STEP(j, 0);
+    FA_O_STEP(j + 1, 1);
+    FA_O_STEP(j + 2, 2);
+    FA_O_STEP(j + 3, 3);
+  }
+  if (j < ntiles) FA_O_STEP(j, 0);
+  if (j + 1 < ntiles) FA_O_STEP(j + 1, 1);
+  if (j + 2 < ntiles) FA_O_STEP(j + 2, 2);
+#undef FA_O_STEP
+  __builtin_amdgcn_s_waitcnt(0);  // no copy may land after the workgroup ends
+  plain_barrier();                // the S waves' last barrier
+  const float l_round = l_round0 + l_round1;
+  const float lr = l_round + swap_halves(l_round, hh);
+  if (my_q >= Sq) return;
+  const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
+  uint16_t* Orow = O + qhead + (size_t)my_q * D;
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      u32x2 pk;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const __bf16 lo = (__bf16)(acc[db][gq * 4 + 2 * t] * inv);
+        const __bf16 hi = (__bf16)(acc[db][gq * 4 + 2 * t + 1] * inv);
+        pk[t] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+                ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+      }
+      *reinterpret_cast<u32x2*>(Orow + db * 32 + gq * 8 + hh * 4) = pk;
+    }
+}
+
+// ----------------------------------------------------------------------------
 // float32 kernel (v_mfma_f32_32x32x2_f32): same tiling and softmax, float32
 // operands and float32 softmax weights.  Single-buffered LDS, 32-key tiles.
 // ----------------------------------------------------------------------------
@@ -1355,7 +1757,8 @@ int launch(KernelT kernel, unsigned grid, unsigned threads, hipStream_t stream, 
 
 // Launch shape of the bf16 kernel for one call.
 struct LaunchCfg {
-  int waves;     // wavefronts per workgroup (32 query rows each)
+  int waves;     // wavefronts per workgroup
+  int rows;      // query rows per workgroup (32 per wave; at D = 256 per pair of waves)
   int bc;        // keys per K/V tile
   int nq;        // query tiles per head
   unsigned grid; // workgroups
@@ -1370,7 +1773,8 @@ struct LaunchCfg {
 // long as themselves, so the longest query tile's keys exceed the mean by at
 // most a third), two per CU otherwise (the causal mask over a square
 // sequence: lengths 1..n).  At D = 64 the exponentials, not the copies,
-// dominate, and D = 256 runs one wave per SIMD.
+// dominate.  D = 256 runs four pairs of waves on 128 rows (two waves per
+// SIMD).
 LaunchCfg bf16_config(int Sq, int Sk, int D, bool causal, int bh_total) {
   constexpr int64_t kCUs = 256;
   LaunchCfg cfg;
@@ -1379,7 +1783,12 @@ LaunchCfg bf16_config(int Sq, int Sk, int D, bool causal, int bh_total) {
   const bool even = !causal || (int64_t)Sk - Sq >= Sq;
   if (D == 128 && (int64_t)((Sq + 255) / 256) * bh_total >= (even ? 1 : 2) * kCUs)
     cfg.waves = 8;
-  const int br = kRowsPerWave * cfg.waves;
+  cfg.rows = kRowsPerWave * cfg.waves;
+  if (D == 256) {
+    cfg.waves = kPipe == kPipeD256Ring ? 4 : 8;
+    cfg.rows = 128;
+  }
+  const int br = cfg.rows;
   cfg.nq = (Sq + br - 1) / br;
   cfg.grid = (unsigned)cfg.nq * (unsigned)bh_total;
   return cfg;
@@ -1393,14 +1802,23 @@ int run_bf16(const void* q, const void* k, const void* v, void* o, float* lse, i
   const uint16_t* K = static_cast<const uint16_t*>(k);
   const uint16_t* V = static_cast<const uint16_t*>(v);
   uint16_t* Out = static_cast<uint16_t*>(o);
-  // the head-dim split copy exists for D = 128 only
-  constexpr int P = kPipe == kPipeKSplit && D != 128 ? kPipeNoPrefetch : kPipe;
-  if constexpr (D == 256) {
+  // the head-dim split copy exists for D = 128 only; the D = 256 study mode
+  // leaves D <= 128 as the library runs it
+  constexpr int P = kPipe == kPipeKSplit && D != 128 ? kPipeNoPrefetch
+                    : kPipe == kPipeD256Ring         ? kPipeOverlap
+                                                     : kPipe;
+  if constexpr (D == 256 && kPipe == kPipeD256Ring) {
     if (causal)
-      return launch(fa_fwd_bf16_ring_kernel<D, BC, WAVES, true>, cfg.grid, 64 * WAVES, stream, Q,
-                    K, V, Out, lse, Sq, Sk, cfg.nq, p.bh_total, p.group_heads, p.c);
-    return launch(fa_fwd_bf16_ring_kernel<D, BC, WAVES, false>, cfg.grid, 64 * WAVES, stream, Q, K,
-                  V, Out, lse, Sq, Sk, cfg.nq, p.bh_total, p.group_heads, p.c);
+      return launch(fa_fwd_bf16_ring_kernel<D, BC, WAVES, true>, cfg.grid, 64 * cfg.waves, stream,
+                    Q, K, V, Out, lse, Sq, Sk, cfg.nq, p.bh_total, p.group_heads, p.c);
+    return launch(fa_fwd_bf16_ring_kernel<D, BC, WAVES, false>, cfg.grid, 64 * cfg.waves, stream,
+                  Q, K, V, Out, lse, Sq, Sk, cfg.nq, p.bh_total, p.group_heads, p.c);
+  } else if constexpr (D == 256) {
+    if (causal)
+      return launch(fa_fwd_bf16_pair_kernel<true>, cfg.grid, 64 * cfg.waves, stream, Q, K, V, Out,
+                    lse, Sq, Sk, cfg.nq, p.bh_total, p.group_heads, p.c);
+    return launch(fa_fwd_bf16_pair_kernel<false>, cfg.grid, 64 * cfg.waves, stream, Q, K, V, Out,
+                  lse, Sq, Sk, cfg.nq, p.bh_total, p.group_heads, p.c);
   } else {
     if (causal)
       return launch(fa_fwd_bf16_kernel<D, BC, WAVES, true, kMfmaSum, P>, cfg.grid, 64 * WAVES, stream,
@@ -1605,7 +2023,7 @@ extern "C" int fa_fwd_plan(int B, int H, int S, int D, int causal, int elem_byte
   int rows, keys, thr, grid;
   if (elem_bytes == 2) {
     const LaunchCfg cfg = bf16_config(S, S, D, causal != 0, bh);
-    rows = kRowsPerWave * cfg.waves;
+    rows = cfg.rows;
     keys = cfg.bc;
     thr = 64 * cfg.waves;
     grid = (int)cfg.grid;
@@ -1628,7 +2046,7 @@ extern "C" int fa_fwd_kv_plan(int B, int H, int Sq, int Sk, int D, int causal,
   const int st = validate_shape(B, H, Sq, Sk, D, causal, 2);
   if (st != FA_OK) return st;
   const LaunchCfg cfg = bf16_config(Sq, Sk, D, causal != 0, B * H);
-  if (rows_per_group) *rows_per_group = kRowsPerWave * cfg.waves;
+  if (rows_per_group) *rows_per_group = cfg.rows;
   if (keys_per_tile) *keys_per_tile = cfg.bc;
   if (threads) *threads = 64 * cfg.waves;
   if (groups) *groups = (int)cfg.grid;

@@ -191,7 +191,8 @@ int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
  * work over sequence length ("FlashAttention-2 Optimizations", parallelism).
  *   rows_per_group : query rows per workgroup
  *   keys_per_tile  : keys per K/V tile staged in on-chip memory
- *   threads        : threads per workgroup
+ *   threads        : threads per workgroup (64 per wavefront; a wavefront
+ *                    owns 32 query rows, at D = 256 in bf16 a pair of them)
  *   groups         : workgroups in the grid
  * For fa_fwd_kv use fa_fwd_kv_plan (with the causal mask the choice also
  * depends on the key count).  Outputs are host pointers; each may be NULL.

@@ -244,7 +244,8 @@ def test_missing_library_raises(tmp_path):
 def test_plan_covers_every_query_row(B, H, S, D, causal, eb):
     p = fa.fa_fwd_plan(B, H, S, D, causal, eb)
     rows, keys, thr, groups = (p["rows_per_group"], p["keys_per_tile"], p["threads"], p["groups"])
-    assert thr % 64 == 0 and rows == 32 * (thr // 64)       # 32 query rows per wavefront
+    # 32 query rows per wavefront; at D = 256 (bf16) per pair of wavefronts
+    assert thr % 64 == 0 and rows == 32 * (thr // 64) // (2 if (D, eb) == (256, 2) else 1)
     assert keys in (32, 64)
     assert groups % (B * H) == 0
     per_head = groups // (B * H)
@@ -282,7 +283,7 @@ def test_plan_workgroup_choice():
     assert fa.fa_fwd_plan(2, 16, 4096, 128, 0, 2)["rows_per_group"] == 256
     assert fa.fa_fwd_plan(1, 32, 16384, 64, 1, 2)["rows_per_group"] == 128
     assert fa.fa_fwd_plan(2, 8, 8192, 256, 1, 2) == dict(
-        rows_per_group=128, keys_per_tile=32, threads=256, groups=16 * 64)
+        rows_per_group=128, keys_per_tile=32, threads=512, groups=16 * 64)
     assert fa.fa_fwd_plan(1, 32, 16384, 128, 1, 4) == dict(
         rows_per_group=128, keys_per_tile=32, threads=256, groups=32 * 128)
 

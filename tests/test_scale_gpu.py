@@ -72,7 +72,7 @@ def test_forward_f32_matches_oracle(tag, mk, D):
     check(o.cpu(), lse.cpu(), o_ref, l_ref, torch.float32, f"f32 scale={scale} D={D}")
 
 
-# B, H, S, D, causal: 128-row and 256-row workgroups, the D = 256 ring kernel
+# B, H, S, D, causal: 128-row and 256-row workgroups, the D = 256 wave-pair kernel
 FLIP_SHAPES = [(1, 3, 333, 128, True), (2, 32, 1000, 128, True), (1, 32, 2048, 128, False),
                (2, 2, 777, 64, True), (1, 4, 600, 256, True)]
 
