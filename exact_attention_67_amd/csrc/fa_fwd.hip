@@ -1781,7 +1781,9 @@ LaunchCfg bf16_config(int Sq, int Sk, int D, bool causal, int bh_total) {
   cfg.bc = D == 256 ? 32 : 64;
   cfg.waves = 4;
   const bool even = !causal || (int64_t)Sk - Sq >= Sq;
-  if (D == 128 && (int64_t)((Sq + 255) / 256) * bh_total >= (even ? 1 : 2) * kCUs)
+  // (With at most 128 queries the upper half of a 256-row tile would stay
+  // empty: decode and short chunks keep 128-row workgroups, two per CU.)
+  if (D == 128 && Sq > 128 && (int64_t)((Sq + 255) / 256) * bh_total >= (even ? 1 : 2) * kCUs)
     cfg.waves = 8;
   cfg.rows = kRowsPerWave * cfg.waves;
   if (D == 256) {

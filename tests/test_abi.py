@@ -263,6 +263,11 @@ def test_kv_plan_workgroup_choice():
     assert fa.fa_fwd_kv_plan(1, 300, 200, 399, 128, 1)["rows_per_group"] == 128
     # no mask: one per CU
     assert fa.fa_fwd_kv_plan(1, 300, 200, 200, 128, 0)["rows_per_group"] == 256
+    # at most 128 queries (decode, short chunks): a 256-row tile would be half
+    # empty, so 128-row workgroups whatever the grid
+    assert fa.fa_fwd_kv_plan(16, 32, 1, 8192, 128, 1)["rows_per_group"] == 128
+    assert fa.fa_fwd_kv_plan(16, 32, 128, 8192, 128, 1)["rows_per_group"] == 128
+    assert fa.fa_fwd_kv_plan(16, 32, 129, 8192, 128, 1)["rows_per_group"] == 256
     # square sizes agree with fa_fwd_plan
     for B, H, S, D, c in ((1, 32, 16384, 128, 1), (1, 16, 4096, 128, 1), (2, 8, 999, 256, 0)):
         assert fa.fa_fwd_kv_plan(B, H, S, S, D, c) == fa.fa_fwd_plan(B, H, S, D, c, 2)
