@@ -88,17 +88,18 @@ typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 
-// D = 256: a row's reference max is only raised when a tile's max exceeds it
-// by more than this many powers of two, so softmax weights stay <= 2^24 (their
-// float32 sums and the O accumulator stay far from overflow, and a bf16
-// weight keeps its relative precision at any magnitude).  A large margin
-// keeps the raises rare even for rows whose scores spread widely.
+// D = 256, one-wave ring kernel (a study build): a row's reference max is
+// only raised when a tile's max exceeds it by more than this many powers of
+// two, so softmax weights stay <= 2^24 (their float32 sums and the O
+// accumulator stay far from overflow, and a bf16 weight keeps its relative
+// precision at any magnitude).  A large margin keeps the raises rare even for
+// rows whose scores spread widely.
 constexpr float kRescaleThreshold = 24.0f;
-// Largest sum of one lane's softmax weights in a tile (32 keys) that the
+// Largest sum of one lane's softmax weights in a tile that the D <= 128
 // kernels accept without moving the row's reference max.
 constexpr float kRowSumLimit = 4096.0f;
-// The same limit for the D = 256 kernel: 2^kRescaleThreshold, so that no
-// weight exceeds 2^24 (a sum within it bounds each of its terms).
+// The same limit for the D = 256 wave-pair kernel: 2^kRescaleThreshold, so
+// that no weight exceeds 2^24 (a sum within it bounds each of its terms).
 constexpr float kPairSumLimit = 16777216.0f;
 
 template <int D_, int BC_, int WAVES_>

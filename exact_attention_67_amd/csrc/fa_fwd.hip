@@ -1,7 +1,9 @@
 // Fused, tiled, exact attention forward for MI355X (gfx950, CDNA4).
 //
 // One workgroup of 4 or 8 wavefronts owns one (query tile of 128 or 256 rows,
-// head, batch); each wavefront owns 32 query rows.  Key/value tiles are
+// head, batch); each wavefront owns 32 query rows (at D = 256 a pair of
+// wavefronts on one SIMD shares them, one forming the softmax weights, the
+// other the P*V product).  Key/value tiles are
 // streamed through LDS with a running (online) softmax, so the seq x seq score
 // matrix only ever exists in registers -- the method of "Profiling in PyTorch
 // (Part 3): Attention is all you profile", section "Why flash attention
@@ -13,7 +15,7 @@
 // discusses overlapping the global-memory copy of the next key block with the
 // math on the current one; here whole K/V tiles are copied one to two tiles
 // ahead, straight from global memory into LDS (no register staging), into
-// double-buffered (a four-deep ring at D = 256) LDS buffers.
+// double-buffered (four buffers each at D = 256) LDS buffers.
 //
 // gfx950 mapping (bf16 path):
 //  * Both contractions run on v_mfma_f32_32x32x16_bf16 in transposed form:
@@ -34,10 +36,10 @@
 //    max is raised only when the weights of a tile would grow too large (D <=
 //    128: a lane's sum of weights in the tile above 2^12, found after the
 //    weights are formed, with P*V deferred by one tile so that it only ever
-//    sees checked weights; D = 256: the tile's row max above the reference by
-//    more than 24 powers of two, checked before the tile's work, with the
-//    rescale outside the loop of tiles), so the rescale of the O accumulator
-//    (wave-uniform) runs on few tiles.  O is normalised by the sum of
+//    sees checked weights; D = 256: the same check against 2^24, the O wave
+//    rescaling O when the reference that comes with the weights moved), so
+//    the rescale of the O accumulator (wave-uniform) runs on few tiles.  O is
+//    normalised by the sum of
 //    the bf16 weights that multiplied V (for D <= 128 formed on the matrix
 //    cores by a 16x16x32 product with a 0/1 operand).
 //  * The 1-D grid is decoded XCD-aware (the 8 XCDs receive workgroups round-
@@ -807,7 +809,8 @@ __device__ __forceinline__ void plain_barrier() {
 }
 
 // ----------------------------------------------------------------------------
-// bf16 kernel with a four-deep K/V ring (used at D = 256)
+// bf16 kernel with a four-deep K/V ring (D = 256, one wave per SIMD; the
+// ring256 study build runs it in place of the wave-pair kernel below)
 // ----------------------------------------------------------------------------
 // At D = 256 a wave needs the whole register file, so each SIMD runs a single
 // wave and nothing hides the start-of-tile copy issue or the wait for copies.
@@ -1154,24 +1157,29 @@ __global__ __launch_bounds__(64 * WAVES, D <= 128 ? 2 : 1) void fa_fwd_bf16_ring
 // ----------------------------------------------------------------------------
 // bf16 kernel on wave pairs (D = 256)
 // ----------------------------------------------------------------------------
-// Eight waves, two per SIMD, in four pairs; pair p owns query rows
-// [32p, 32p + 32) of the workgroup's 128.  The S wave of a pair (waves 0-3)
-// forms the scores, the row maxima and the softmax weights; the O wave (waves
-// 4-7, on the same SIMD as its S wave) accumulates O from the weights and V,
-// and issues every K/V tile copy.  Each does 16 of the 32 matrix-core
-// products of a 32-key tile, so neither repeats work, and the S wave's
-// exponentials overlap the O wave's products on the SIMD.  The weights P(t)
-// of tile t (bf16, the B operand of the P.V product exactly as the S wave
-// holds it) pass through LDS with the reference max they were taken against;
-// the O wave rescales O when that reference moved.
+// At D = 256 a wave that held a 32-row slice's whole state (Q, S, O) would
+// need the full register file, one wave per SIMD, and could not hide its own
+// latencies.  Here eight waves, two per SIMD, form four pairs; pair p owns
+// query rows [32p, 32p + 32) of the workgroup's 128.  The S wave of a pair
+// (waves 0-3) holds Q and forms the scores, the softmax weights and their
+// float32 row sum (for the LSE); the O wave (waves 4-7, on the same SIMD as
+// its S wave) holds O, accumulates it from the weights and V, keeps the
+// bf16-weight row sum (the normalisation) and issues every K/V tile copy.
+// Each does 16 of the 32 matrix-core products of a 32-key tile, so neither
+// repeats work, and the S wave's exponentials overlap the O wave's products
+// on the SIMD.  The weights P(t) of tile t (bf16, the B operand of the P.V
+// product exactly as the S wave holds it) pass through LDS with the
+// reference max they were taken against; the O wave rescales O (and its sum)
+// when that reference moved.
 //
 // Step j (one workgroup barrier each): the S wave forms S(j+3) from K(j+3)
 // and the weights P(j+2) of S(j+2); the O wave adds V(j) P(j), with P(j) in
 // registers since step j-1, and reads P(j+1) for the next step, so that no
 // LDS wait sits between the barrier and its first product.  It also issues
 // the copies of K(j+5) and V(j+3), each waited for at the end of step j+1.
-// K and V each have four LDS buffers.  Softmax: as in the ring kernel
-// (reference max from tile 0, raised only past kRescaleThreshold).
+// K and V each have four LDS buffers.  Softmax: the reference max comes from
+// tile 0 and is raised, to the row max seen so far, only when a lane's sum of
+// a tile's weights exceeds kPairSumLimit (no weight above 2^24).
 template <bool CAUSAL>
 __global__ __launch_bounds__(512, 1) void fa_fwd_bf16_pair_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
