@@ -47,7 +47,9 @@
 //    they share its L2) and, when causal, heaviest query tiles first.
 //  * Queries against a longer or shorter key sequence (Sq != Sk, causal mask
 //    aligned bottom-right) run through the same kernels; rows with no visible
-//    key give O = 0 and LSE = -inf.
+//    key give O = 0 and LSE = -inf.  A single query row of few heads
+//    (decode) has a kernel of its own that streams K/V rows into registers
+//    (fa_decode_kernel).
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -1763,6 +1765,184 @@ int launch(KernelT kernel, unsigned grid, unsigned threads, hipStream_t stream, 
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
+// ----------------------------------------------------------------------------
+// bf16 decode kernel: one query row per (batch, head)
+// ----------------------------------------------------------------------------
+// With a single query row the products are matrix-vector ones and the launch
+// is bound by reading K and V from memory.  One workgroup per (batch, head);
+// its WAVES waves take contiguous ranges of the keys and stream them straight
+// from global memory into registers (no LDS staging, so the bytes in flight
+// are bounded by registers, not by LDS buffers): per block of KPI keys, lane l
+// holds head-dim entries [32 (l mod LPK), +32) of key l / LPK (LPK = D / 32
+// lanes per key; consecutive lanes read consecutive 16-byte pieces of
+// consecutive key rows), and the next block's loads are in flight while the
+// current one is used.  Score: bf16 dot products with float32 accumulation,
+// summed over the key's LPK lanes.  Softmax as in the D = 256 wave-pair
+// kernel: the wave's reference max comes from its first block and is raised
+// (to the max of the block) only when a weight would exceed 2^24.  O accumulates the
+// float32 weights times V in float32 and is normalised by the float32 sum of
+// the same weights.  The waves' partial results (reference, sum, O) are then
+// combined through LDS: each weighted by 2^((m_w - m) c) against the largest
+// reference m.  A row always sees every key (the causal mask with one query
+// aligned bottom-right keeps all of them).
+constexpr int kDecodeWaves = 8;
+
+template <int D>
+struct DecCfg {
+  static constexpr int LPK = D / 32;      // lanes per key
+  static constexpr int KPI = 64 / LPK;    // keys per block (one per lane group)
+};
+
+template <int D, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void fa_decode_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE, int Sk,
+    int chunk, float c) {
+  using C = DecCfg<D>;
+  constexpr int LPK = C::LPK, KPI = C::KPI;
+  static_assert(WAVES <= 16 && KPI * LPK == 64, "decode: lane layout");
+  // negative scale: S from -Q with |c| (see kZeroScaleC)
+  const uint32_t qflip = sign_flip_mask(c);
+  c = fabsf(c);
+  __shared__ float wm[WAVES], wl[WAVES];
+  __shared__ float wo[WAVES][D];
+
+  const int bh = blockIdx.x;
+  const uint16_t* Kh = K + (size_t)bh * (size_t)Sk * D;
+  const uint16_t* Vh = V + (size_t)bh * (size_t)Sk * D;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kg = lane / LPK;  // the lane's key within a block
+  const int dg = lane % LPK;  // the lane's 32 head-dim entries
+  const int k_begin = min(Sk, wave * chunk);
+  const int k_end = min(Sk, k_begin + chunk);
+  const int nblk = (k_end - k_begin + KPI - 1) / KPI;
+
+  // the lane's 32 entries of q as bf16 pairs
+  u32x4 qv[4];
+  {
+    const u32x4* qp = reinterpret_cast<const u32x4*>(Q + (size_t)bh * D + dg * 32);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qv[i] = qp[i] ^ qflip;
+  }
+  // loads of block b: the lane's 64 bytes of K and of V (key clamped to the
+  // range; keys past it are masked)
+  const auto load = [&](int b, u32x4 (&kr)[4], u32x4 (&vr)[4]) {
+    const int key = min(k_begin + b * KPI + kg, k_end - 1);
+    const u32x4* kp = reinterpret_cast<const u32x4*>(Kh + (size_t)key * D + dg * 32);
+    const u32x4* vp = reinterpret_cast<const u32x4*>(Vh + (size_t)key * D + dg * 32);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kr[i] = kp[i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vr[i] = vp[i];
+  };
+  // sum over the lanes of a key, max over the keys of the block
+  const auto key_sum = [&](float x) {
+#pragma unroll
+    for (int msk = 1; msk < LPK; msk <<= 1) x += __shfl_xor(x, msk);
+    return x;
+  };
+  const auto block_max = [&](float x) {
+#pragma unroll
+    for (int msk = LPK; msk < 64; msk <<= 1) x = fmaxf(x, __shfl_xor(x, msk));
+    return x;
+  };
+
+  float o[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) o[i] = 0.0f;
+  float l = 0.0f;          // the lane's key weights summed (each key once per lane)
+  float m_ref = -INFINITY;  // the wave's reference max (raw scores)
+
+  const auto block = [&](int b, const u32x4 (&kr)[4], const u32x4 (&vr)[4]) {
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // (element copies first: a bit cast of a vector element would read element 0)
+        const uint32_t kk = kr[i][e], qq = qv[i][e];
+        s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, kk),
+                                            __builtin_bit_cast(bf16x2, qq), s, false);
+      }
+    s = key_sum(s);
+    if (k_begin + b * KPI + kg >= k_end) s = -INFINITY;
+    if (b == 0) m_ref = block_max(s);  // finite: the block holds key k_begin
+    float p = fast_exp2(fmaf(s, c, -m_ref * c));
+    if (__any(!(p <= kPairSumLimit))) {
+      const float m_new = fmaxf(m_ref, block_max(s));
+      const float alpha = fast_exp2((m_ref - m_new) * c);
+      m_ref = m_new;
+      l *= alpha;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) o[i] *= alpha;
+      p = fast_exp2(fmaf(s, c, -m_ref * c));
+    }
+    l += p;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t w = vr[i][e];
+        o[8 * i + 2 * e] = fmaf(p, __builtin_bit_cast(float, w << 16), o[8 * i + 2 * e]);
+        o[8 * i + 2 * e + 1] =
+            fmaf(p, __builtin_bit_cast(float, w & 0xffff0000u), o[8 * i + 2 * e + 1]);
+      }
+  };
+
+  if (nblk > 0) {
+    // loads are unconditional (a key past the range reads the range's last
+    // row again); only the blocks' arithmetic stops at nblk
+    u32x4 k0[4], v0[4], k1[4], v1[4];
+    load(0, k0, v0);
+    for (int b = 0; b < nblk; b += 2) {
+      load(b + 1, k1, v1);
+      block(b, k0, v0);
+      load(b + 2, k0, v0);
+      if (b + 1 < nblk) block(b + 1, k1, v1);
+    }
+    // the wave's totals: O over the keys of the block (lanes of equal dg), l
+#pragma unroll
+    for (int i = 0; i < 32; ++i)
+#pragma unroll
+      for (int msk = LPK; msk < 64; msk <<= 1) o[i] += __shfl_xor(o[i], msk);
+#pragma unroll
+    for (int msk = LPK; msk < 64; msk <<= 1) l += __shfl_xor(l, msk);
+  }
+  if (lane == 0) {
+    wm[wave] = m_ref;
+    wl[wave] = l;
+  }
+  if (kg == 0) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) wo[wave][dg * 32 + i] = o[i];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  float m = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < WAVES; ++w) m = fmaxf(m, wm[w]);
+  float lt = 0.0f;
+  float f[WAVES];
+#pragma unroll
+  for (int w = 0; w < WAVES; ++w) {
+    f[w] = wm[w] == -INFINITY ? 0.0f : fast_exp2((wm[w] - m) * c);
+    lt += wl[w] * f[w];
+  }
+  const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+  constexpr int DPL = D / 64;  // output entries per lane
+  uint16_t* Orow = O + (size_t)bh * D;
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) {
+    const int d = lane * DPL + i;
+    float acc = 0.0f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) acc = fmaf(wo[w][d], f[w], acc);
+    Orow[d] = __builtin_bit_cast(uint16_t, (__bf16)(acc * inv));
+  }
+  if (lane == 0) LSE[bh] = (m * c + fast_log2(lt)) * kLn2;
+}
+
 // Launch shape of the bf16 kernel for one call.
 struct LaunchCfg {
   int waves;     // wavefronts per workgroup
@@ -1770,6 +1950,7 @@ struct LaunchCfg {
   int bc;        // keys per K/V tile
   int nq;        // query tiles per head
   unsigned grid; // workgroups
+  bool decode;   // fa_decode_kernel: one query row, one workgroup per head
 };
 
 // Tile sizes: 64-key tiles up to D = 128, 32-key tiles at D = 256 (LDS and
@@ -1782,10 +1963,23 @@ struct LaunchCfg {
 // most a third), two per CU otherwise (the causal mask over a square
 // sequence: lengths 1..n).  At D = 64 the exponentials, not the copies,
 // dominate.  D = 256 runs four pairs of waves on 128 rows (two waves per
-// SIMD).
+// SIMD).  A single query row against the keys of at most one head per CU
+// (D <= 128) goes to fa_decode_kernel: with so few workgroups the tiled
+// kernel's one staged tile per wave keeps too few bytes in flight per CU,
+// while the decode kernel's eight waves each hold two blocks of K/V rows in
+// registers.  With more heads the two read at about the same rate.
 LaunchCfg bf16_config(int Sq, int Sk, int D, bool causal, int bh_total) {
   constexpr int64_t kCUs = 256;
   LaunchCfg cfg;
+  cfg.decode = Sq == 1 && D <= 128 && bh_total <= kCUs;
+  if (cfg.decode) {
+    cfg.waves = kDecodeWaves;
+    cfg.rows = 1;
+    cfg.bc = 2048 / D;  // keys per block of the decode kernel
+    cfg.nq = 1;
+    cfg.grid = (unsigned)bh_total;
+    return cfg;
+  }
   cfg.bc = D == 256 ? 32 : 64;
   cfg.waves = 4;
   const bool even = !causal || (int64_t)Sk - Sq >= Sq;
@@ -1839,6 +2033,17 @@ int run_bf16(const void* q, const void* k, const void* v, void* o, float* lse, i
 }
 
 template <int D>
+int run_decode(const void* q, const void* k, const void* v, void* o, float* lse, int Sk,
+               const Plan& p, const LaunchCfg& cfg, hipStream_t stream) {
+  constexpr int KPI = DecCfg<D>::KPI;
+  // contiguous key ranges of whole blocks, one per wave
+  const int chunk = (int)(((int64_t)Sk + kDecodeWaves * KPI - 1) / (kDecodeWaves * KPI) * KPI);
+  return launch(fa_decode_kernel<D, kDecodeWaves>, cfg.grid, 64 * kDecodeWaves, stream,
+                static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, Sk, chunk, p.c);
+}
+
+template <int D>
 int run_f32(const float* q, const float* k, const float* v, float* o, float* lse, int S,
             bool causal, const Plan& p, hipStream_t stream) {
   const int nq = (S + kBr - 1) / kBr;
@@ -1857,6 +2062,9 @@ int fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, i
   if (st != FA_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const LaunchCfg cfg = bf16_config(Sq, Sk, D, causal, p.bh_total);
+  if (cfg.decode)
+    return D == 64 ? run_decode<64>(q, k, v, o, lse, Sk, p, cfg, s)
+                   : run_decode<128>(q, k, v, o, lse, Sk, p, cfg, s);
   switch (D) {
     case 64: return run_bf16<64, 64, 4>(q, k, v, o, lse, Sq, Sk, causal, p, cfg, s);
     case 128:

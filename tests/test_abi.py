@@ -240,10 +240,16 @@ def test_missing_library_raises(tmp_path):
 @pytest.mark.parametrize("B,H,S,D,causal,eb", [
     (1, 32, 16384, 128, 1, 2), (2, 16, 4096, 128, 1, 2), (2, 16, 4096, 128, 0, 2),
     (1, 16, 4096, 128, 1, 2), (4, 16, 1024, 64, 1, 2), (2, 8, 8192, 256, 1, 2),
-    (1, 2, 128, 64, 1, 4), (3, 5, 1, 128, 0, 2), (7, 3, 257, 256, 0, 4), (32, 16, 300, 128, 1, 2)])
+    (1, 2, 128, 64, 1, 4), (3, 5, 1, 128, 0, 2), (7, 3, 257, 256, 0, 4), (32, 16, 300, 128, 1, 2),
+    (3, 5, 1, 64, 1, 2), (3, 5, 1, 256, 1, 2), (3, 5, 1, 128, 1, 4), (16, 17, 1, 128, 0, 2)])
 def test_plan_covers_every_query_row(B, H, S, D, causal, eb):
     p = fa.fa_fwd_plan(B, H, S, D, causal, eb)
     rows, keys, thr, groups = (p["rows_per_group"], p["keys_per_tile"], p["threads"], p["groups"])
+    if S == 1 and eb == 2 and D <= 128 and B * H <= 256:
+        # the decode kernel: one workgroup of 8 wavefronts per head, blocks of
+        # 2048 / D keys
+        assert (rows, keys, thr, groups) == (1, 2048 // D, 512, B * H)
+        return
     # 32 query rows per wavefront; at D = 256 (bf16) per pair of wavefronts
     assert thr % 64 == 0 and rows == 32 * (thr // 64) // (2 if (D, eb) == (256, 2) else 1)
     assert keys in (32, 64)
@@ -268,6 +274,13 @@ def test_kv_plan_workgroup_choice():
     assert fa.fa_fwd_kv_plan(16, 32, 1, 8192, 128, 1)["rows_per_group"] == 128
     assert fa.fa_fwd_kv_plan(16, 32, 128, 8192, 128, 1)["rows_per_group"] == 128
     assert fa.fa_fwd_kv_plan(16, 32, 129, 8192, 128, 1)["rows_per_group"] == 256
+    # one query row of at most one head per CU, D <= 128: the decode kernel
+    assert fa.fa_fwd_kv_plan(4, 32, 1, 8192, 128, 1) == dict(
+        rows_per_group=1, keys_per_tile=16, threads=512, groups=128)
+    assert fa.fa_fwd_kv_plan(8, 32, 1, 8192, 64, 0) == dict(
+        rows_per_group=1, keys_per_tile=32, threads=512, groups=256)
+    assert fa.fa_fwd_kv_plan(1, 257, 1, 8192, 128, 1)["rows_per_group"] == 128
+    assert fa.fa_fwd_kv_plan(4, 32, 1, 8192, 256, 1)["rows_per_group"] == 128
     # square sizes agree with fa_fwd_plan
     for B, H, S, D, c in ((1, 32, 16384, 128, 1), (1, 16, 4096, 128, 1), (2, 8, 999, 256, 0)):
         assert fa.fa_fwd_kv_plan(B, H, S, S, D, c) == fa.fa_fwd_plan(B, H, S, D, c, 2)

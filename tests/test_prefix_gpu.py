@@ -132,6 +132,56 @@ def test_fwd_kv_prefix_single_round_of_256_row_workgroups():
 
 
 # ---------------------------------------------------------------------------
+# The decode kernel: one query row of at most 256 heads, D <= 128
+# ---------------------------------------------------------------------------
+
+DECODE_CASES = [  # B, H, Sk, D
+    (1, 3, 1, 128),       # a single key: seven of the eight waves get none
+    (2, 3, 7, 64),        # fewer keys than waves
+    (1, 4, 127, 128),     # one partial block per wave
+    (2, 5, 1000, 64),     # ragged last block
+    (3, 7, 4099, 128),    # several blocks per wave, ragged
+    (1, 2, 40000, 64),    # long prefix
+    (4, 64, 8192, 128),   # 256 heads: the largest grid the decode kernel takes
+]
+
+
+@pytest.mark.parametrize("B,H,Sk,D", DECODE_CASES,
+                         ids=[f"B{B}H{H}-k{Sk}-D{D}" for B, H, Sk, D in DECODE_CASES])
+def test_decode_kernel_parity(B, H, Sk, D):
+    assert fa.fa_fwd_kv_plan(B, H, 1, Sk, D, 1)["rows_per_group"] == 1
+    q, k, v = _qkv(B, H, 1, Sk, D, seed=9000 + Sk + D)
+    s = _scale(D)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    o, lse = fa.forward_kv(qd, kd, vd, causal=True, scale=s)
+    o_n, lse_n = fa.forward_kv(qd, kd, vd, causal=False, scale=s)
+    torch.cuda.synchronize()
+    # one query aligned bottom-right sees every key: both masks, same launch
+    assert torch.equal(o, o_n) and torch.equal(lse, lse_n)
+    heads = [(b, h) for b in range(B) for h in range(H)]
+    if len(heads) > 16:
+        heads = heads[::len(heads) // 16]
+    for b, h in heads:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        o_ref, l_ref = pre.attention_prefix(q[sl], k[sl], v[sl], True, s)
+        check(o[sl], lse[sl], o_ref, l_ref, f"decode B={B} H={H} Sk={Sk} D={D} b={b} h={h}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("scale", [-0.125, 0.0, 1.0, 3.0])
+def test_decode_kernel_other_scales(D, scale):
+    # negative (scores of -Q), zero (uniform weights) and large scales; at
+    # 1.0 and 3.0 later keys outweigh a wave's first block by far more than
+    # 2^24, so the reference max is raised during the pass
+    B, H, Sk = 2, 3, 3000
+    q, k, v = _qkv(B, H, 1, Sk, D, seed=9500 + D)
+    o, lse = fa.forward_kv(q.cuda(), k.cuda(), v.cuda(), causal=True, scale=scale)
+    torch.cuda.synchronize()
+    o_ref, l_ref = pre.attention_prefix(q, k, v, True, scale)
+    check(o, lse, o_ref, l_ref, f"decode scale={scale} D={D}")
+
+
+# ---------------------------------------------------------------------------
 # Compositions through fa_merge
 # ---------------------------------------------------------------------------
 
