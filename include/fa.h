@@ -194,6 +194,10 @@ int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
  *   threads        : threads per workgroup (64 per wavefront; a wavefront
  *                    owns 32 query rows, at D = 256 in bf16 a pair of them)
  *   groups         : workgroups in the grid
+ * A single query row (S = 1 here, Sq = 1 for fa_fwd_kv) of at most 256
+ * (batch, head) pairs with D <= 128 in bf16 runs the decode kernel instead:
+ * rows_per_group = 1, keys_per_tile = 2048 / D keys read per block into
+ * registers (not staged), threads = 512, groups = B * H.
  * For fa_fwd_kv use fa_fwd_kv_plan (with the causal mask the choice also
  * depends on the key count).  Outputs are host pointers; each may be NULL.
  * Returns FA_ERR_SHAPE, FA_ERR_HEADDIM or FA_ERR_CAUSAL where fa_fwd would
