@@ -131,6 +131,22 @@ def test_fwd_kv_prefix_single_round_of_256_row_workgroups():
         check(o[sl], lse[sl], o_ref, l_ref, f"kv prefix one round h={h}")
 
 
+@pytest.mark.parametrize("name", list(wl.PREFIX_WORKLOADS))
+def test_prefix_workloads_full_size_sampled_heads(name):
+    # the prefill and decode workloads the benchmark times, at full size and in
+    # the launch it times; sampled heads against the oracle
+    w = wl.PREFIX_WORKLOADS[name]
+    q, k, v = wl.make_prefix_inputs(w)
+    o, lse = fa.forward_kv(q.cuda(), k.cuda(), v.cuda(), causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    heads = [(0, 0), (w.B - 1, w.H - 1)] if w.Sq > 1 else [(0, 0), (w.B // 2, 7), (w.B - 1, w.H - 1)]
+    for b, h in heads:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        o_ref, l_ref = pre.attention_prefix(q[sl], k[sl], v[sl], w.causal, w.scale)
+        check(o[sl], lse[sl], o_ref, l_ref, f"{name} b={b} h={h}")
+
+
 # ---------------------------------------------------------------------------
 # The decode kernel: one query row of at most 256 heads, D <= 128
 # ---------------------------------------------------------------------------

@@ -141,6 +141,9 @@ PREFIX_WORKLOADS: Dict[str, PrefixWorkload] = {
         "prefill_bf16_causal_1x32_q2048_k16384_d128", 1, 32, 2048, 16384, 128, True, 11),
     "decode_bf16_causal_16x32_q1_k8192_d128": PrefixWorkload(
         "decode_bf16_causal_16x32_q1_k8192_d128", 16, 32, 1, 8192, 128, True, 12),
+    # few heads, long prefix: the same K/V bytes on 128 heads
+    "decode_bf16_causal_4x32_q1_k32768_d128": PrefixWorkload(
+        "decode_bf16_causal_4x32_q1_k32768_d128", 4, 32, 1, 32768, 128, True, 13),
 }
 
 
