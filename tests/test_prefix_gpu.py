@@ -184,6 +184,31 @@ def test_decode_kernel_parity(B, H, Sk, D):
 
 
 @pytest.mark.parametrize("D", [64, 128])
+def test_decode_kernel_outputs_guarded_and_deterministic(D):
+    # outputs poisoned with NaN between sentinel bands: every O and LSE element
+    # written (finite), nothing beyond them; a second call gives the same bits
+    B, H, Sk, pad = 3, 5, 1000, 4096
+    assert fa.fa_fwd_kv_plan(B, H, 1, Sk, D, 1)["rows_per_group"] == 1
+    q, k, v = (t.cuda() for t in _qkv(B, H, 1, Sk, D, seed=9700 + D))
+    n, nl = B * H * D, B * H
+    obuf = torch.full((n + 2 * pad,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lbuf = torch.full((nl + 2 * pad,), float("nan"), dtype=torch.float32, device="cuda")
+    for buf in (obuf, lbuf):
+        buf[:pad] = 7.0
+        buf[-pad:] = 7.0
+    o = obuf[pad:pad + n].view(B, H, 1, D)
+    lse = lbuf[pad:pad + nl].view(B, H, 1)
+    fa.forward_kv(q, k, v, causal=True, out=o, lse=lse)
+    first = (o.clone(), lse.clone())
+    fa.forward_kv(q, k, v, causal=True, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(first[0]).all()) and bool(torch.isfinite(first[1]).all())
+    assert bool((obuf[:pad] == 7).all()) and bool((obuf[-pad:] == 7).all())
+    assert bool((lbuf[:pad] == 7).all()) and bool((lbuf[-pad:] == 7).all())
+    assert torch.equal(first[0], o) and torch.equal(first[1], lse)
+
+
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("scale", [-0.125, 0.0, 1.0, 3.0])
 def test_decode_kernel_other_scales(D, scale):
     # negative (scores of -Q), zero (uniform weights) and large scales; at
