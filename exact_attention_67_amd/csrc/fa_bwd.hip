@@ -13,8 +13,7 @@
 //   dS    = P * (dP - Delta)
 //   dq    = scale * dS k,   dk = scale * dS^T q
 //
-// Three kernels:
-//  * fa_bwd_delta_kernel: Delta (one row per TPR consecutive lanes).
+// Two kernels, dQ first:
 //  * fa_bwd_dkdv_pair_kernel: one workgroup of 8 wavefronts per (block of
 //    128 keys, head, batch).  Waves w and w + 4 share a SIMD and own the same
 //    32 keys; the P wave forms S = q K^T, the weights P and dV, and hands P
@@ -31,6 +30,8 @@
 //    S^T = K q^T, dP^T = V dO^T, dS^T, then dq^T += K^T dS^T with K read
 //    transposed.  K and V tiles are stored in one swizzle that serves both the
 //    row reads and the transposing reads, so each K tile is copied once.
+//    Before its loop it forms Delta for its rows from the dO fragments it
+//    holds and O loaded the same way, and stores it for dK/dV.
 // No atomics and no workspace beyond the caller's Delta buffer: dq is
 // accumulated by the workgroup that owns the query tile.  fa_bwd_noalloc
 // keeps Delta in a fixed device array of the library instead (scratch below).
@@ -46,35 +47,6 @@
 #include "fa_device.h"
 
 namespace {
-
-// ----------------------------------------------------------------------------
-// Delta = rowsum(dO * O)
-// ----------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void fa_bwd_delta_kernel(const uint16_t* __restrict__ O,
-                                                           const uint16_t* __restrict__ dO,
-                                                           float* __restrict__ Delta,
-                                                           int64_t rows) {
-  constexpr int TPR = D / 8;  // lanes per row, 8 elements (16 bytes) each
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t r = t / TPR;
-  const int c = (int)(t % TPR);
-  float acc = 0.0f;
-  if (r < rows) {
-    const u32x4 a = *reinterpret_cast<const u32x4*>(O + r * D + c * 8);
-    const u32x4 b = *reinterpret_cast<const u32x4*>(dO + r * D + c * 8);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc = fmaf(__builtin_bit_cast(float, a[e] << 16), __builtin_bit_cast(float, b[e] << 16), acc);
-      acc = fmaf(__builtin_bit_cast(float, a[e] & 0xFFFF0000u),
-                 __builtin_bit_cast(float, b[e] & 0xFFFF0000u), acc);
-    }
-  }
-  // sum over the TPR consecutive lanes of the row (all lanes take part)
-#pragma unroll
-  for (int m = TPR / 2; m > 0; m >>= 1) acc += __shfl_xor(acc, m);
-  if (r < rows && c == 0) Delta[r] = acc;
-}
 
 // Copy of 64 floats (one per query row of a tile) into LDS: lane l copies
 // src[min(row0 + l, S - 1)].
@@ -484,8 +456,9 @@ template <int D, int BC, int WAVES, bool CAUSAL>
 __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 2 : 1) void fa_bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-    const float* __restrict__ LSE, const float* __restrict__ Delta, uint16_t* __restrict__ dQ,
-    int S, int nq, int bh_total, int group_heads, float c, float scale) {
+    const uint16_t* __restrict__ O, const float* __restrict__ LSE, float* __restrict__ Delta,
+    uint16_t* __restrict__ dQ, int S, int nq, int bh_total, int group_heads, float c,
+    float scale) {
   using C = BfCfg<D, BC, WAVES>;  // key tiles of BC; waves of 32 queries
   // K tile in two layouts (row reads for S^T, transposed reads for dq), V
   // tile row-wise (for dP^T); two stages.
@@ -542,7 +515,20 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 2 : 1) void fa_bwd_dq_kern
   int k_off[C::NKOFF], v_off[C::NVOFF], v_hi[C::NVOFF];
   operand_offsets_u<C>(lane, k_off, v_off, v_hi);
   const float lse2 = my_q < S ? LSE[(size_t)bh * S + my_q] * kLog2e : 0.0f;
-  const float delta = my_q < S ? Delta[(size_t)bh * S + my_q] : 0.0f;
+  // Delta of the wave's rows, from the dO fragments and O loaded the same
+  // way (each lane half holds half of a row's entries); stored for dK/dV.
+  float delta;
+  {
+    bf16x8 of[C::KCH];
+    row_fragments<C>(of, O + head, my_q, S, hh);
+    float part = 0.0f;
+#pragma unroll
+    for (int ch = 0; ch < C::KCH; ++ch)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part = fmaf((float)df[ch][e], (float)of[ch][e], part);
+    delta = part + __shfl_xor(part, 32);
+    if (hh == 0 && my_q < S) Delta[(size_t)bh * S + my_q] = delta;
+  }
 
   f32x16 acc[C::DB];
 #pragma unroll
@@ -611,32 +597,31 @@ template <int D>
 int run_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
             const uint16_t* dout, const float* lse, uint16_t* dq, uint16_t* dk, uint16_t* dv,
             float* delta, int bh, int S, bool causal, float scale, hipStream_t s) {
-  const int64_t rows = (int64_t)bh * S;
   const float c = scale == 0.0f ? kZeroScaleC : scale * kLog2e;  // sign: see kZeroScaleC
   const int group_heads = bh >= 8 ? bh / 8 : 1;
-  int st = launch_k(fa_bwd_delta_kernel<D>, (unsigned)((rows * (D / 8) + 255) / 256), 256, s,
-                    o, dout, delta, rows);
-  if (st != FA_OK) return st;
-  // dQ: 8 waves and 64-key tiles; D = 256: 4 waves and 32-key tiles
-  // (registers and LDS).
+  // dQ first: it also forms Delta, which dK/dV reads.  dQ: 8 waves and
+  // 64-key tiles; D = 256: 4 waves and 32-key tiles (registers and LDS).
   constexpr int BT = D == 256 ? 32 : 64;
   constexpr int QW = D == 256 ? 4 : 8;
+  const int nq = (S + 32 * QW - 1) / (32 * QW);
+  const unsigned gq = (unsigned)nq * (unsigned)bh;
+  int st;
+  if (causal)
+    st = launch_k(fa_bwd_dq_kernel<D, BT, QW, true>, gq, 64 * QW, s, q, k, v, dout, o,
+                  (const float*)lse, delta, dq, S, nq, bh, group_heads, c, scale);
+  else
+    st = launch_k(fa_bwd_dq_kernel<D, BT, QW, false>, gq, 64 * QW, s, q, k, v, dout, o,
+                  (const float*)lse, delta, dq, S, nq, bh, group_heads, c, scale);
+  if (st != FA_OK) return st;
   const int nk = (S + 127) / 128;
   const unsigned grid = (unsigned)nk * (unsigned)bh;
   if (causal)
-    st = launch_k(fa_bwd_dkdv_pair_kernel<D, true>, grid, 512, s, q, k, v, dout,
-                  (const float*)lse, (const float*)delta, dk, dv, S, nk, bh, group_heads, c, scale);
-  else
-    st = launch_k(fa_bwd_dkdv_pair_kernel<D, false>, grid, 512, s, q, k, v, dout,
-                  (const float*)lse, (const float*)delta, dk, dv, S, nk, bh, group_heads, c, scale);
-  if (st != FA_OK) return st;
-  const int nq = (S + 32 * QW - 1) / (32 * QW);
-  const unsigned gq = (unsigned)nq * (unsigned)bh;
-  if (causal)
-    return launch_k(fa_bwd_dq_kernel<D, BT, QW, true>, gq, 64 * QW, s, q, k, v, dout,
-                    (const float*)lse, (const float*)delta, dq, S, nq, bh, group_heads, c, scale);
-  return launch_k(fa_bwd_dq_kernel<D, BT, QW, false>, gq, 64 * QW, s, q, k, v, dout,
-                  (const float*)lse, (const float*)delta, dq, S, nq, bh, group_heads, c, scale);
+    return launch_k(fa_bwd_dkdv_pair_kernel<D, true>, grid, 512, s, q, k, v, dout,
+                    (const float*)lse, (const float*)delta, dk, dv, S, nk, bh, group_heads, c,
+                    scale);
+  return launch_k(fa_bwd_dkdv_pair_kernel<D, false>, grid, 512, s, q, k, v, dout,
+                  (const float*)lse, (const float*)delta, dk, dv, S, nk, bh, group_heads, c,
+                  scale);
 }
 
 }  // namespace
@@ -696,8 +681,8 @@ int bwd(const void* q, const void* k, const void* v, const void* o, const void* 
 }
 
 // Delta of fa_bwd_noalloc: one float per query row, at most FA_BWD_SCRATCH_ROWS
-// rows per call.  Every row a call uses is written by fa_bwd_delta_kernel
-// before the other kernels of that call read it, so nothing needs clearing.
+// rows per call.  Every row a call uses is written by the call's dQ kernel
+// before its dK/dV kernel reads it, so nothing needs clearing.
 // Each GPU holds its own copy of the array, at its own address, for the life
 // of the process; host code uses that address (scratch_address), never the
 // array's name, which on the host only stands in for the device symbol.
