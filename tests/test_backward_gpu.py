@@ -119,6 +119,31 @@ def test_backward_tensors_beyond_4gib():
     torch.cuda.empty_cache()
 
 
+FULL = [("c3_bf16_2x16x4096x128", False, [(0, 0), (1, 15)]),
+        ("c3_bf16_2x16x4096x128", True, [(0, 0), (1, 15)]),
+        ("c4_bf16_causal_1x32x16384x128", True, [(0, 31)]),
+        ("c5_bf16_causal_2x8x8192x256_stress", True, [(1, 7)])]
+
+
+@pytest.mark.parametrize("name,causal,heads", FULL,
+                         ids=[f"{n}-{'c' if c else 'n'}" for n, c, _ in FULL])
+def test_backward_full_size_sampled_heads(name, causal, heads):
+    # the backward the benchmark times, at full size and in its launch
+    # configuration (dO drawn as the benchmark draws it); whole gradients of
+    # sampled heads against the oracle on those heads
+    w = wl.WORKLOADS[name]
+    q, k, v = wl.make_inputs(w)
+    g = torch.Generator("cpu").manual_seed(w.seed + 100)
+    do = torch.randn(q.shape, generator=g).to(torch.bfloat16)
+    _, _, dq, dk, dv = run_backward(q, k, v, do, causal, w.scale)
+    torch.cuda.empty_cache()
+    for b, h in heads:
+        sl = lambda t: t[b:b + 1, h:h + 1]
+        ref = bwd.attention_backward(sl(q), sl(k), sl(v), sl(do), causal, w.scale)
+        check_grads((sl(dq), sl(dk), sl(dv)), ref, f"bwd {name} causal={causal} b={b} h={h}")
+        del ref
+
+
 def test_delta_buffer_is_rowsum():
     B, H, S, D = 1, 2, 200, 128
     q, k, v = (t.cuda() for t in wl.make_qkv(B, H, S, D, torch.bfloat16, seed=15000))
