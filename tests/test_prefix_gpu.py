@@ -183,6 +183,28 @@ def test_decode_kernel_parity(B, H, Sk, D):
         check(o[sl], lse[sl], o_ref, l_ref, f"decode B={B} H={H} Sk={Sk} D={D} b={b} h={h}")
 
 
+def test_decode_kernel_keys_beyond_4gib():
+    # K and V larger than 4 GiB each (the last head's keys lie more than 2^32
+    # bytes past the base); the first and last heads against the oracle
+    # (inputs drawn on the GPU from a seeded generator, those heads copied back)
+    B, H, Sk, D = 1, 256, 66536, 128
+    assert H * Sk * D * 2 > (1 << 32)
+    assert fa.fa_fwd_kv_plan(B, H, 1, Sk, D, 1)["rows_per_group"] == 1
+    g = torch.Generator(device="cuda").manual_seed(9800)
+    q = torch.randn((B, H, 1, D), generator=g, device="cuda", dtype=torch.bfloat16)
+    k = torch.randn((B, H, Sk, D), generator=g, device="cuda", dtype=torch.bfloat16)
+    v = torch.randn((B, H, Sk, D), generator=g, device="cuda", dtype=torch.bfloat16)
+    s = _scale(D)
+    o, lse = fa.forward_kv(q, k, v, causal=True, scale=s)
+    torch.cuda.synchronize()
+    for h in (0, H - 1):
+        sl = (slice(0, 1), slice(h, h + 1))
+        o_ref, l_ref = pre.attention_prefix(q[sl].cpu(), k[sl].cpu(), v[sl].cpu(), True, s)
+        check(o[sl].cpu(), lse[sl].cpu(), o_ref, l_ref, f"decode >4GiB h={h}")
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("D", [64, 128])
 def test_decode_kernel_outputs_guarded_and_deterministic(D):
     # outputs poisoned with NaN between sentinel bands: every O and LSE element
