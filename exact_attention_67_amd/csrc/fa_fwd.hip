@@ -1772,19 +1772,20 @@ int launch(KernelT kernel, unsigned grid, unsigned threads, hipStream_t stream, 
 // is bound by reading K and V from memory.  One workgroup per (batch, head);
 // its WAVES waves take contiguous ranges of the keys and stream them straight
 // from global memory into registers (no LDS staging, so the bytes in flight
-// are bounded by registers, not by LDS buffers): per block of KPI keys, lane l
-// holds head-dim entries [32 (l mod LPK), +32) of key l / LPK (LPK = D / 32
-// lanes per key; consecutive lanes read consecutive 16-byte pieces of
-// consecutive key rows), and the next block's loads are in flight while the
-// current one is used.  Score: bf16 dot products with float32 accumulation,
-// summed over the key's LPK lanes.  Softmax as in the D = 256 wave-pair
-// kernel: the wave's reference max comes from its first block and is raised
-// (to the max of the block) only when a weight would exceed 2^24.  O accumulates the
-// float32 weights times V in float32 and is normalised by the float32 sum of
-// the same weights.  The waves' partial results (reference, sum, O) are then
-// combined through LDS: each weighted by 2^((m_w - m) c) against the largest
-// reference m.  A row always sees every key (the causal mask with one query
-// aligned bottom-right keeps all of them).
+// are bounded by registers, not by LDS buffers).  Per block of KPI keys, lane
+// l holds head-dim entries [32 (l mod LPK), +32) of key l / LPK (LPK = D / 32
+// lanes per key): 64 contiguous bytes of K and of V per lane, and one
+// contiguous range of KPI rows per wave.  The next block's loads are in
+// flight while the current one is used.  Score: bf16 dot products with
+// float32 accumulation, summed over the key's LPK lanes.  Softmax as in the
+// D = 256 wave-pair kernel: the wave's reference max comes from its first
+// block and is raised (to the max of the block) only when a weight would
+// exceed 2^24.  O accumulates the float32 weights (not rounded) times V in
+// float32 and is normalised by the float32 sum of the same weights.  The
+// waves' partial results (reference, sum, O) are then combined through LDS,
+// each weighted by 2^((m_w - m) c) against the largest reference m.  A row
+// always sees every key (the causal mask with one query aligned bottom-right
+// keeps all of them).
 constexpr int kDecodeWaves = 8;
 
 template <int D>
